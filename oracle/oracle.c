@@ -1,0 +1,307 @@
+/*
+ * Reference oracle for the sparse top-K mixture-of-experts feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct CPU
+ * statement of what the layer computes.  Only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load it.  It shares no code, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * Arithmetic: every product and sum is done in IEEE double.  Inputs arrive as
+ * float arrays (a bf16 value widens to float exactly, and float widens to
+ * double exactly), so no input is rounded.  Nothing intermediate is rounded.
+ *
+ * Sources (the pages on "Mixtral of Experts", arXiv 2401.04088):
+ *   [G]  xyznot digest, section "Method (with core equations)": the gate
+ *        G(x) := Softmax(TopK(x . W_g)), where TopK keeps the K largest entries
+ *        of the logit vector l = x . W_g (n entries) and sets the rest to -inf.
+ *   [Y]  same section: y = sum over i = 0..n-1 of G(x)_i * SwiGLU_i(x).
+ *   [S]  same page, "Key terms": SwiGLU is a gated linear unit combining the
+ *        Swish activation with an elementwise product; same section: each
+ *        expert is a SwiGLU block with intermediate size 14336, n = 8, K = 2.
+ *   [Z]  GeekNews summary, "Cara Komputasi Layer MoE": experts whose gate is
+ *        zero need not be computed; the softmax is taken over the top-K logits
+ *        of a linear layer.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - SwiGLU_i(u) = W2_i (SiLU(W1_i u) (*) W3_i u), Swish with beta = 1 (SiLU),
+ *     no biases.  The SiLU branch is W1.
+ *   - Exactly K experts survive TopK; among equal logits the lower expert
+ *     index ranks first.  Slot 0 holds the largest logit.
+ *   - Storage: x[T][d], W_g[d][n] (column i belongs to expert i),
+ *     W1,W3[n][d_ff][d], W2[n][d][d_ff], y[T][d], all row-major.
+ *   - Block variant (a layer of a stack, not on the pages): u = x / sqrt(mean(x^2)
+ *     + eps) with unit weight, y = x + MoE(u).
+ *
+ * Parallelism: OpenMP over tokens only.  Each token is computed by exactly the
+ * per-token definition, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Swish with beta = 1 ([S]): z * sigmoid(z). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Stack-layer pre-normalisation (not on the pages): u = x / sqrt(mean(x^2) + eps),
+ * unit weight. */
+static void rms_normalize(const float* x, int64_t d, double eps, double* u) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < d; ++k) ss += (double)x[k] * (double)x[k];
+    const double inv = 1.0 / sqrt(ss / (double)d + eps);
+    for (int64_t k = 0; k < d; ++k) u[k] = (double)x[k] * inv;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* [G]: logits l_i = sum_k x_k W_g[k][i] for one token. */
+static void token_logits(const float* x, const float* Wg, int64_t d, int32_t n,
+                         double* l) {
+    for (int32_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int64_t k = 0; k < d; ++k) s += (double)x[k] * (double)Wg[k * n + i];
+        l[i] = s;
+    }
+}
+
+/* [G]: TopK.  Repeatedly take the largest logit not yet taken; a strictly
+ * larger value is needed to displace an earlier (lower-index) candidate, so
+ * ties go to the lower index.  Returns the K chosen experts in rank order. */
+static void topk_select(const double* l, int32_t n, int32_t K, int32_t* sel) {
+    unsigned char taken[4096];
+    memset(taken, 0, (size_t)n);
+    for (int32_t j = 0; j < K; ++j) {
+        int32_t best = -1;
+        for (int32_t i = 0; i < n; ++i) {
+            if (taken[i]) continue;
+            if (best < 0 || l[i] > l[best]) best = i;
+        }
+        sel[j] = best;
+        taken[best] = 1;
+    }
+}
+
+/* [G]: Softmax over the TopK-masked vector.  Masked entries are exp(-inf) = 0,
+ * so only the K kept logits enter; m is subtracted for range only. */
+static void masked_softmax(const double* l, const int32_t* sel, int32_t K,
+                           double* g) {
+    double m = l[sel[0]];
+    for (int32_t j = 1; j < K; ++j)
+        if (l[sel[j]] > m) m = l[sel[j]];
+    double z = 0.0;
+    for (int32_t j = 0; j < K; ++j) {
+        g[j] = exp(l[sel[j]] - m);
+        z += g[j];
+    }
+    for (int32_t j = 0; j < K; ++j) g[j] /= z;
+}
+
+/* [S]: one expert, o = W2 (SiLU(W1 u) (*) W3 u).  h has d_ff entries. */
+static void swiglu_expert(const double* u, const float* W1, const float* W3,
+                          const float* W2, int64_t d, int64_t d_ff, double* h,
+                          double* o) {
+    for (int64_t f = 0; f < d_ff; ++f) {
+        double a = 0.0, b = 0.0;
+        const float* w1 = W1 + f * d;
+        const float* w3 = W3 + f * d;
+        for (int64_t k = 0; k < d; ++k) {
+            a += (double)w1[k] * u[k];
+            b += (double)w3[k] * u[k];
+        }
+        h[f] = silu(a) * b;
+    }
+    for (int64_t c = 0; c < d; ++c) {
+        double s = 0.0;
+        const float* w2 = W2 + c * d_ff;
+        for (int64_t f = 0; f < d_ff; ++f) s += (double)w2[f] * h[f];
+        o[c] = s;
+    }
+}
+
+/* One token of the layer: route, then [Y] y = sum_j g_j SwiGLU_{s_j}(u).
+ * Experts off the selection have gate exactly 0 ([Z]) and are skipped.
+ * If forced is non-null it replaces the TopK choice (used to evaluate the
+ * other valid choice when two logits tie within a tolerance). */
+static void token_forward(const double* u, const float* Wg,
+                          const float* W1, const float* W3, const float* W2,
+                          int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                          const int32_t* forced, double* y, int32_t* idx_out,
+                          double* gate_out, double* logit_out, double* scratch) {
+    double* l = scratch;            /* n */
+    double* h = l + n;              /* d_ff */
+    double* o = h + d_ff;           /* d */
+    double g[64];
+    int32_t sel[64] = {0};
+    for (int32_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int64_t k = 0; k < d; ++k) s += u[k] * (double)Wg[k * n + i];
+        l[i] = s;
+    }
+    if (forced) {
+        for (int32_t j = 0; j < K; ++j) sel[j] = forced[j];
+    } else {
+        topk_select(l, n, K, sel);
+    }
+    masked_softmax(l, sel, K, g);
+    for (int64_t c = 0; c < d; ++c) y[c] = 0.0;
+    for (int32_t j = 0; j < K; ++j) {
+        const int64_t e = sel[j];
+        swiglu_expert(u, W1 + e * d_ff * d, W3 + e * d_ff * d, W2 + e * d * d_ff,
+                      d, d_ff, h, o);
+        for (int64_t c = 0; c < d; ++c) y[c] += g[j] * o[c];
+    }
+    if (idx_out)
+        for (int32_t j = 0; j < K; ++j) idx_out[j] = sel[j];
+    if (gate_out)
+        for (int32_t j = 0; j < K; ++j) gate_out[j] = g[j];
+    if (logit_out)
+        for (int32_t i = 0; i < n; ++i) logit_out[i] = l[i];
+}
+
+/* Router only ([G]): logits[T][n], idx[T][K], gate[T][K].  Any output may be
+ * NULL.  Returns 0, or -1 on invalid sizes. */
+int oracle_route(const float* x, const float* Wg, int64_t T, int64_t d, int32_t n,
+                 int32_t K, double* logits, int32_t* idx, double* gate) {
+    if (T < 0 || d <= 0 || n <= 0 || n > 4096 || K <= 0 || K > n || K > 64)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double lbuf[4096];
+        double g[64];
+        int32_t sel[64];
+        token_logits(x + t * d, Wg, d, n, lbuf);
+        topk_select(lbuf, n, K, sel);
+        masked_softmax(lbuf, sel, K, g);
+        if (logits)
+            for (int32_t i = 0; i < n; ++i) logits[t * n + i] = lbuf[i];
+        if (idx)
+            for (int32_t j = 0; j < K; ++j) idx[t * K + j] = sel[j];
+        if (gate)
+            for (int32_t j = 0; j < K; ++j) gate[t * K + j] = g[j];
+    }
+    return 0;
+}
+
+/* Whole layer ([G], [Y], [S]) on the tokens listed in rows[0..R) (all T tokens
+ * when rows is NULL, R = T).  Output row r of y/idx/gate/logits belongs to
+ * token rows[r].  forced (nullable) is [R][K] expert ids replacing TopK.
+ * Returns 0, -1 on invalid sizes, -2 on allocation failure. */
+int oracle_forward(const float* x, const float* Wg, const float* W1, const float* W3,
+                   const float* W2, int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                   int32_t K, const int64_t* rows, int64_t R, const int32_t* forced,
+                   double* y, int32_t* idx, double* gate, double* logits) {
+    if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n)
+        return -1;
+    if (!rows) R = T;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)(n + d_ff + 2 * d));
+        if (!scratch) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+            double* u = scratch + n + d_ff + d;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < R; ++r) {
+                const int64_t t = rows ? rows[r] : r;
+                for (int64_t k = 0; k < d; ++k) u[k] = (double)x[t * d + k];
+                token_forward(u, Wg, W1, W3, W2, d, d_ff, n, K,
+                              forced ? forced + r * K : 0, y + r * d,
+                              idx ? idx + r * K : 0, gate ? gate + r * K : 0,
+                              logits ? logits + r * n : 0, scratch);
+            }
+            free(scratch);
+        }
+    }
+    return err;
+}
+
+/* One layer of a stack (not on the pages; the stack workload's definition):
+ * u = x / sqrt(mean(x^2) + eps) (unit weight), y = x + MoE(u).  Same row
+ * selection and forced-routing conventions as oracle_forward; idx/gate/logits
+ * describe the routing of u. */
+int oracle_block_forward(const float* x, const float* Wg, const float* W1,
+                         const float* W3, const float* W2, int64_t T, int64_t d,
+                         int64_t d_ff, int32_t n, int32_t K, double eps,
+                         const int64_t* rows, int64_t R, const int32_t* forced,
+                         double* y, int32_t* idx, double* gate, double* logits) {
+    if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n ||
+        !(eps >= 0.0))
+        return -1;
+    if (!rows) R = T;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)(n + d_ff + 2 * d));
+        if (!scratch) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+            double* u = scratch + n + d_ff + d;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < R; ++r) {
+                const int64_t t = rows ? rows[r] : r;
+                const float* xt = x + t * d;
+                rms_normalize(xt, d, eps, u);
+                double* yr = y + r * d;
+                token_forward(u, Wg, W1, W3, W2, d, d_ff, n, K,
+                              forced ? forced + r * K : 0, yr,
+                              idx ? idx + r * K : 0, gate ? gate + r * K : 0,
+                              logits ? logits + r * n : 0, scratch);
+                for (int64_t k = 0; k < d; ++k) yr[k] += (double)xt[k];
+            }
+            free(scratch);
+        }
+    }
+    return err;
+}
+
+/* Routing of a stack layer: TopK/Softmax of RMSNorm(x) . W_g on every token.
+ * Same outputs as oracle_route. */
+int oracle_block_route(const float* x, const float* Wg, int64_t T, int64_t d,
+                       int32_t n, int32_t K, double eps, double* logits,
+                       int32_t* idx, double* gate) {
+    if (T < 0 || d <= 0 || n <= 0 || n > 64 || K <= 0 || K > n || !(eps >= 0.0))
+        return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* u = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!u) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                double l[64], g[64];
+                int32_t sel[64] = {0};
+                rms_normalize(x + t * d, d, eps, u);
+                for (int32_t i = 0; i < n; ++i) {
+                    double s = 0.0;
+                    for (int64_t k = 0; k < d; ++k) s += u[k] * (double)Wg[k * n + i];
+                    l[i] = s;
+                }
+                topk_select(l, n, K, sel);
+                masked_softmax(l, sel, K, g);
+                if (logits)
+                    for (int32_t i = 0; i < n; ++i) logits[t * n + i] = l[i];
+                if (idx)
+                    for (int32_t j = 0; j < K; ++j) idx[t * K + j] = sel[j];
+                if (gate)
+                    for (int32_t j = 0; j < K; ++j) gate[t * K + j] = g[j];
+            }
+            free(u);
+        }
+    }
+    return err;
+}

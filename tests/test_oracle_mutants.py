@@ -1,0 +1,67 @@
+"""The pins must be able to fail: plant plausible mistakes in a copy of the
+oracle's C source (on the CPU, in a temporary directory), build the mutant, and
+check that at least one pin in tests/test_oracle_pins.py rejects it."""
+import os
+import subprocess
+
+import pytest
+
+import oracle as oracle_pkg
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
+
+MUTANTS = {
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "swap_w1_w3": ("h[f] = silu(a) * b;", "h[f] = silu(b) * a;"),
+    "tie_to_higher_index": ("if (best < 0 || l[i] > l[best]) best = i;",
+                            "if (best < 0 || l[i] >= l[best]) best = i;"),
+    "softmax_sign": ("g[j] = exp(l[sel[j]] - m);", "g[j] = exp(m - l[sel[j]]);"),
+    "router_transposed": ("s += u[k] * (double)Wg[k * n + i];",
+                          "s += u[k] * (double)Wg[i * d + k];"),
+    "down_transposed": ("const float* w2 = W2 + c * d_ff;\n        for (int64_t f = 0; f < d_ff; ++f) s += (double)w2[f] * h[f];",
+                        "for (int64_t f = 0; f < d_ff; ++f) s += (double)W2[f * d + c] * h[f];"),
+    "gate_dropped": ("y[c] += g[j] * o[c];", "y[c] += o[c];"),
+    "expert_stride": ("W1 + e * d_ff * d, W3 + e * d_ff * d", "W1 + e * d_ff, W3 + e * d_ff"),
+    "rms_mean": ("ss / (double)d + eps", "ss + eps"),
+    "residual_dropped": ("yr[k] += (double)xt[k];", "yr[k] += 0.0;"),
+    "second_slot_gate": ("for (int32_t j = 0; j < K; ++j) g[j] /= z;",
+                         "for (int32_t j = 0; j < K; ++j) g[j] /= (j ? z : 1.0);"),
+}
+
+PIN_TESTS = [
+    lambda o: pins.test_dense_mixture_when_K_equals_n(o),
+    lambda o: pins.test_single_expert_is_swiglu_ffn(o),
+    lambda o: pins.test_silu_branch_closed_form(o),
+    lambda o: pins.test_gates_nonnegative_normalised_ordered(o),
+    lambda o: pins.test_two_way_softmax_is_logistic(o),
+    lambda o: pins.test_logits_match_library_matmul(o),
+    lambda o: pins.test_bruteforce_selection_and_output(o, 8, 2),
+    lambda o: pins.test_sparse_equals_dense_with_zero_gates(o),
+    lambda o: pins.test_zero_token(o),
+    lambda o: pins.test_duplicate_router_columns_tie_to_lower_index(o),
+    lambda o: pins.test_block_layer_is_residual_over_rmsnorm(o),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site of {name} not found"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o",
+                    str(so_path), str(c_path), "-lm"], check=True)
+    monkeypatch.setattr(oracle_pkg, "_LIB_PATH", str(so_path))
+    monkeypatch.setattr(oracle_pkg, "_lib", None)
+    caught = 0
+    for pin in PIN_TESTS:
+        try:
+            pin(oracle_pkg)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    monkeypatch.setattr(oracle_pkg, "_lib", None)
+    assert caught > 0, f"no pin rejects the mutant {name}"
