@@ -1,0 +1,144 @@
+/*
+ * moe.h -- C ABI of libmoe.so, a gfx950 (MI355X) implementation of the sparse
+ * top-K mixture-of-experts feed-forward layer of "Mixtral of Experts"
+ * (arXiv 2401.04088).
+ *
+ * What the layer computes (xyznot digest of the paper, section "Method (with
+ * core equations)"; GeekNews summary, section "Cara Komputasi Layer MoE"):
+ *
+ *   l    = x . W_g                       router logits, one per expert (n of them)
+ *   G(x) = Softmax(TopK(l))              TopK keeps the K largest logits and sets
+ *                                        the others to -inf, so the softmax runs
+ *                                        over the K kept logits only
+ *   y    = sum_i G(x)_i * SwiGLU_i(x)    experts with a zero gate are not run
+ *   SwiGLU_i(u) = W2_i (SiLU(W1_i u) (*) W3_i u),  SiLU(z) = z / (1 + e^-z)
+ *
+ * Readings this library fixes where the pages are silent:
+ *   - exactly K experts are kept; among equal logits the lower index ranks
+ *     first; slot 0 of a token's (idx, gate) pair holds the largest logit;
+ *   - router logits are accumulated in fp32 and never rounded to bf16;
+ *   - bf16 path: products accumulate in fp32; the SwiGLU hidden activation is
+ *     rounded to bf16 before the down projection; expert outputs stay fp32
+ *     until the gate-weighted sum, which is rounded once (RNE) into y.
+ *
+ * Layouts (all row-major, contiguous, device memory, 16-byte aligned):
+ *   x    [T][d]           activations (dtype dt)
+ *   W_g  [d][n]           router weight; column i belongs to expert i
+ *   W1   [n][d_ff][d]     gate projection (SiLU branch), [out][in]
+ *   W3   [n][d_ff][d]     up projection, [out][in]
+ *   W2   [n][d][d_ff]     down projection, [out][in]
+ *   y    [T][d]           output (dtype dt)
+ *   idx  [T][K] int32, gate [T][K] float
+ *
+ * Ownership and side effects: every pointer is owned by the caller.  Inputs
+ * are never written.  y is fully overwritten and must not overlap any input
+ * or the workspace.  The library keeps no pointer after a call returns and
+ * never allocates device memory; scratch space comes from the caller's
+ * workspace, whose contents are undefined afterwards.
+ *
+ * Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream).  No call synchronises the host with the device.
+ *
+ * Errors: arguments are validated before anything is enqueued, so a call that
+ * returns an error other than MOE_ERR_HIP has had no effect.  MOE_ERR_HIP
+ * reports a launch failure (hipGetLastError); a fault inside a kernel shows
+ * up at the caller's next synchronisation instead.  No C++ exception crosses
+ * this boundary.  moe_last_error() returns a thread-local description of the
+ * most recent failure on the calling thread.
+ *
+ * Supported on the GPU: 1 <= n <= 64, 1 <= K <= min(n, 8), d and d_ff
+ * multiples of 8, T * K < 2^31, dtype MOE_F32 or MOE_BF16.  T = 0 is a no-op
+ * that returns MOE_OK.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, aliasing */
+    MOE_ERR_UNSUPPORTED = 2,      /* valid layer, but outside what the GPU path supports */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+} moe_status_t;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,  /* fp32 storage, fp32 arithmetic */
+    MOE_BF16 = 1  /* bf16 storage, fp32 accumulation */
+} moe_dtype_t;
+
+/* Version of this ABI (MOE_ABI_VERSION of the library that was built). */
+int32_t moe_abi_version(void);
+
+/* Router only: the gating equation of the "Method" section.  Writes, for
+ * every token t, idx[t][0..K) (experts in rank order: largest logit first,
+ * ties to the lower index) and gate[t][0..K) (softmax over the K kept logits,
+ * each >= 0, summing to 1).  Needs no workspace. */
+moe_status_t moe_route(const void* x, const void* w_g, int64_t T, int64_t d,
+                       int32_t n, int32_t K, moe_dtype_t dt, int32_t* idx,
+                       float* gate, void* stream);
+
+/* Token permutation ("experts with zero gate need not be computed": each
+ * expert gets the contiguous list of the assignments routed to it).  Input
+ * idx[T][K]; assignment a = t*K + k goes to expert idx[a].  Output:
+ *   offsets[n+1]  offsets[e] = first position of expert e, offsets[n] = T*K
+ *   perm[T*K]     perm[pos] = a, positions of one expert in increasing a
+ *                 (a stable counting sort by expert)
+ *   inv[T*K]      inv[a] = pos (the inverse of perm)
+ * Every idx entry must lie in [0, n); the result is unspecified otherwise. */
+moe_status_t moe_permute(const int32_t* idx, int64_t T, int32_t n, int32_t K,
+                         int32_t* offsets, int32_t* perm, int32_t* inv,
+                         void* stream);
+
+/* Bytes of workspace that moe_forward and moe_block_forward need for these
+ * sizes.  An upper bound that does not depend on how tokens get routed.
+ * Returns 0 if the sizes are invalid. */
+size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                           int32_t K, moe_dtype_t dt);
+
+/* The whole layer, y = sum_i G(x)_i SwiGLU_i(x) (output equation of the
+ * "Method" section).  workspace: device memory of at least
+ * moe_workspace_bytes(...) bytes, 256-byte aligned.  Optional outputs (NULL to
+ * skip): idx_out[T][K], gate_out[T][K] -- the routing that was used -- and
+ * counts_out[n], the number of assignments each expert received. */
+moe_status_t moe_forward(const void* x, const void* w_g, const void* w1,
+                         const void* w3, const void* w2, int64_t T, int64_t d,
+                         int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
+                         void* y, void* workspace, size_t workspace_bytes,
+                         int32_t* idx_out, float* gate_out, int32_t* counts_out,
+                         void* stream);
+
+/* One layer of a pre-normalised residual stack (the MoE replaces every
+ * feed-forward sub-block, "Core ideas" of the xyznot digest; the
+ * normalisation and residual are this workload's definition, not the
+ * pages'):
+ *   u = x / sqrt(mean(x^2) + eps)   (unit weight; routing uses u in fp32)
+ *   y = x + MoE(u)                  (residual added in fp32, rounded once)
+ * Same arguments and outputs as moe_forward plus eps (>= 0). */
+moe_status_t moe_block_forward(const void* x, const void* w_g, const void* w1,
+                               const void* w3, const void* w2, int64_t T,
+                               int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                               moe_dtype_t dt, float eps, void* y, void* workspace,
+                               size_t workspace_bytes, int32_t* idx_out,
+                               float* gate_out, int32_t* counts_out,
+                               void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

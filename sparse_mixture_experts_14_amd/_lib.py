@@ -1,0 +1,202 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: torch device tensors become raw pointers, the
+current torch stream becomes the hipStream_t, and every step of the layer runs
+in the library's HIP kernels.  There is no fallback: if libmoe.so is missing
+or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_HIP = 4
+MOE_F32 = 0
+MOE_BF16 = 1
+
+EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
+           "moe_forward", "moe_block_forward", "moe_status_string", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libmoe.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m sparse_mixture_experts_14_amd.build`")
+    lib = ctypes.CDLL(p)
+    V, I64, I32, SZ, F = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
+                          ctypes.c_float)
+    lib.moe_abi_version.restype = I32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route.argtypes = [V, V, I64, I64, I32, I32, ctypes.c_int, V, V, V]
+    lib.moe_permute.restype = ctypes.c_int
+    lib.moe_permute.argtypes = [V, I64, I32, I32, V, V, V, V]
+    lib.moe_workspace_bytes.restype = SZ
+    lib.moe_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, ctypes.c_int]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, V, V, SZ,
+                                V, V, V, V]
+    lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_block_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, F,
+                                      V, V, SZ, V, V, V, V]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(st: int, fn: str):
+    if st != MOE_OK:
+        lib = load()
+        raise MoeError(st, fn, lib.moe_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int, dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_workspace_bytes(T, d, d_ff, n, K, code))
+
+
+def route(x: torch.Tensor, Wg: torch.Tensor, K: int):
+    """(idx[T][K] int32, gate[T][K] float32) of the router on every token."""
+    T, d = x.shape
+    n = Wg.shape[1]
+    if Wg.shape[0] != d or Wg.dtype != x.dtype:
+        raise ValueError("W_g must be [d][n] with the dtype of x")
+    idx = torch.empty(T, K, dtype=torch.int32, device=x.device)
+    gate = torch.empty(T, K, dtype=torch.float32, device=x.device)
+    st = load().moe_route(_dev(x, "x"), _dev(Wg, "W_g"), T, d, n, K, _dtype_code(x),
+                          idx.data_ptr(), gate.data_ptr(), _stream(x.device))
+    _check(st, "moe_route")
+    return idx, gate
+
+
+def permute(idx: torch.Tensor, n: int):
+    """(offsets[n+1], perm[T*K], inv[T*K]) of the stable counting sort."""
+    T, K = idx.shape
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    offsets = torch.empty(n + 1, dtype=torch.int32, device=idx.device)
+    perm = torch.empty(T * K, dtype=torch.int32, device=idx.device)
+    inv = torch.empty(T * K, dtype=torch.int32, device=idx.device)
+    st = load().moe_permute(_dev(idx, "idx"), T, n, K, offsets.data_ptr(), perm.data_ptr(),
+                            inv.data_ptr(), _stream(idx.device))
+    _check(st, "moe_permute")
+    return offsets, perm, inv
+
+
+class Layer:
+    """A reusable call site: owns the workspace for one (T, d, d_ff, n, K,
+    dtype) and the optional routing outputs."""
+
+    def __init__(self, T, d, d_ff, n, K, dtype, device, routing_outputs=True):
+        self.T, self.d, self.d_ff, self.n, self.K = T, d, d_ff, n, K
+        self.dtype = dtype
+        self.device = torch.device(device)
+        nbytes = workspace_bytes(T, d, d_ff, n, K, dtype)
+        if nbytes == 0 and T > 0:
+            raise ValueError("invalid layer sizes")
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.ws_bytes = nbytes
+        if routing_outputs:
+            self.idx = torch.empty(T, K, dtype=torch.int32, device=self.device)
+            self.gate = torch.empty(T, K, dtype=torch.float32, device=self.device)
+            self.counts = torch.empty(n, dtype=torch.int32, device=self.device)
+        else:
+            self.idx = self.gate = self.counts = None
+
+    def _args(self, x, Wg, W1, W3, W2):
+        T, d, d_ff, n, K = self.T, self.d, self.d_ff, self.n, self.K
+        if x.shape != (T, d) or Wg.shape != (d, n) or W1.shape != (n, d_ff, d) \
+                or W3.shape != (n, d_ff, d) or W2.shape != (n, d, d_ff):
+            raise ValueError("tensor shapes do not match the layer sizes")
+        for t in (Wg, W1, W3, W2):
+            if t.dtype != x.dtype:
+                raise ValueError("all inputs must share one dtype")
+        if x.dtype != self.dtype:
+            raise ValueError("dtype differs from the layer's")
+        return (_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"), _dev(W2, "W2"))
+
+    def forward(self, x, Wg, W1, W3, W2, out=None):
+        y = out if out is not None else torch.empty_like(x)
+        px = self._args(x, Wg, W1, W3, W2)
+        st = load().moe_forward(*px, self.T, self.d, self.d_ff, self.n, self.K,
+                                _dtype_code(x), _dev(y, "y"), self.workspace.data_ptr(),
+                                self.ws_bytes, _ptr(self.idx), _ptr(self.gate),
+                                _ptr(self.counts), _stream(x.device))
+        _check(st, "moe_forward")
+        return y
+
+    def block_forward(self, x, Wg, W1, W3, W2, eps, out=None):
+        y = out if out is not None else torch.empty_like(x)
+        px = self._args(x, Wg, W1, W3, W2)
+        st = load().moe_block_forward(*px, self.T, self.d, self.d_ff, self.n, self.K,
+                                      _dtype_code(x), float(eps), _dev(y, "y"),
+                                      self.workspace.data_ptr(), self.ws_bytes, _ptr(self.idx),
+                                      _ptr(self.gate), _ptr(self.counts), _stream(x.device))
+        _check(st, "moe_block_forward")
+        return y
+
+
+def forward(x, Wg, W1, W3, W2, K: int):
+    """y of the layer; returns (y, idx, gate, counts)."""
+    n, d_ff, d = W1.shape
+    L = Layer(x.shape[0], d, d_ff, n, K, x.dtype, x.device)
+    y = L.forward(x, Wg, W1, W3, W2)
+    return y, L.idx, L.gate, L.counts
+
+
+def block_forward(x, Wg, W1, W3, W2, K: int, eps: float):
+    """y = x + MoE(RMSNorm(x)); returns (y, idx, gate, counts)."""
+    n, d_ff, d = W1.shape
+    L = Layer(x.shape[0], d, d_ff, n, K, x.dtype, x.device)
+    y = L.block_forward(x, Wg, W1, W3, W2, eps)
+    return y, L.idx, L.gate, L.counts

@@ -1,0 +1,306 @@
+// C ABI of libmoe.so: validation, workspace layout, launch sequence.
+//
+// Layer of "Mixtral of Experts" (xyznot digest, "Method (with core equations)"):
+// G(x) = Softmax(TopK(x . W_g)),  y = sum_i G(x)_i SwiGLU_i(x).
+// Launch sequence on the caller's stream, no host synchronisation:
+//   router -> permute -> gate/up grouped GEMM -> down grouped GEMM -> combine
+// Arguments are checked before anything is enqueued; see include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status_t hip_fail(hipError_t err, const char* where) {
+    return fail(MOE_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(err), (int)err);
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;   // keeps in-kernel int index math exact
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Which GEMM kernels run for these sizes, and how many K splits the down
+// projection uses.  Depends on sizes only (so the workspace bound holds); the
+// environment variable MOE_GEMM_PATH=tiled|skinny forces a bf16 path (a
+// testing and tuning knob).
+// K splits of the skinny down projection: more workgroups when there are
+// few rows (decode), none otherwise.
+int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 4 : 1; }
+
+struct Plan {
+    bool skinny;
+    int down_splits;  // partial sums of the down projection (skinny path)
+};
+
+Plan choose_plan(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt) {
+    Plan p{false, 1};
+    if (dt != MOE_BF16) return p;
+    const int64_t A = T * K;
+    // expected rows per expert; the skinny kernel re-streams weights per 16 rows
+    p.skinny = A <= 16 * (int64_t)n;
+    if (const char* f = getenv("MOE_GEMM_PATH")) {
+        if (!strcmp(f, "tiled")) p.skinny = false;
+        if (!strcmp(f, "skinny")) p.skinny = true;
+    }
+    // splits requested; the launcher may use fewer (never more) when d_ff is short
+    if (p.skinny) p.down_splits = requested_down_splits(T, K);
+    (void)d;
+    (void)d_ff;
+    return p;
+}
+
+struct Layout {
+    size_t idx, gate, offsets, perm, inv, u, H, O, total;
+};
+
+Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt) {
+    const size_t A = (size_t)T * (size_t)K;
+    const size_t es = dt == MOE_BF16 ? 2 : 4;
+    const int S = requested_down_splits(T, K);  // upper bound of the splits used
+    Layout L{};
+    size_t o = 0;
+    L.idx = o;     o = align256(o + A * 4);
+    L.gate = o;    o = align256(o + A * 4);
+    L.offsets = o; o = align256(o + (size_t)(n + 1) * 4);
+    L.perm = o;    o = align256(o + A * 4);
+    L.inv = o;     o = align256(o + A * 4);
+    L.u = o;       o = align256(o + (size_t)T * (size_t)d * es);
+    L.H = o;       o = align256(o + A * (size_t)d_ff * es);
+    L.O = o;       o = align256(o + (size_t)S * A * (size_t)d * 4);
+    L.total = o;
+    return L;
+}
+
+moe_status_t check_sizes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                         moe_dtype_t dt, bool need_ff) {
+    if (dt != MOE_F32 && dt != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+    if (d <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "d = %lld <= 0", (long long)d);
+    if (need_ff && d_ff <= 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "d_ff = %lld <= 0", (long long)d_ff);
+    if (n <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "n = %d <= 0", n);
+    if (K <= 0 || K > n) return fail(MOE_ERR_INVALID_ARGUMENT, "K = %d outside [1, n=%d]", K, n);
+    if (n > 64) return fail(MOE_ERR_UNSUPPORTED, "n = %d > 64", n);
+    if (K > 8) return fail(MOE_ERR_UNSUPPORTED, "K = %d > 8", K);
+    if (d % 8 != 0 || d > kMaxDim)
+        return fail(MOE_ERR_UNSUPPORTED, "d = %lld must be a multiple of 8 and <= 2^24",
+                    (long long)d);
+    if (need_ff && (d_ff % 8 != 0 || d_ff > kMaxDim))
+        return fail(MOE_ERR_UNSUPPORTED, "d_ff = %lld must be a multiple of 8 and <= 2^24",
+                    (long long)d_ff);
+    if (T > kMaxRows / K)
+        return fail(MOE_ERR_UNSUPPORTED, "T * K = %lld * %d >= 2^31", (long long)T, K);
+    return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
+}
+
+moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
+                           const void* w3, const void* w2, int64_t T, int64_t d,
+                           int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, float eps,
+                           void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
+                           float* gate_out, int32_t* counts_out, void* stream) {
+    const char* fn = block ? "moe_block_forward" : "moe_forward";
+    moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
+    if (st != MOE_OK) return st;
+    if (block && !(eps >= 0.0f && eps < 1e30f))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    const void* ptrs[] = {x, w_g, w1, w3, w2, y};
+    const char* names[] = {"x", "w_g", "w1", "w3", "w2", "y"};
+    for (int i = 0; i < 6; ++i) {
+        if (!ptrs[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
+        if (!aligned(ptrs[i], 16))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
+    }
+    if ((idx_out && !aligned(idx_out, 4)) || (gate_out && !aligned(gate_out, 4)) ||
+        (counts_out && !aligned(counts_out, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: optional outputs must be 4-byte aligned", fn);
+    if (dt == MOE_F32 && (int64_t)T * K / 64 + n > 65535)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 path supports T * K < 4M", fn);
+    const Layout L = layout(T, d, d_ff, n, K, dt);
+    if (T > 0) {
+        if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
+        if (!aligned(workspace, 256))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
+        if (ws_bytes < L.total)
+            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", fn,
+                        ws_bytes, L.total);
+    }
+    const size_t es = dt == MOE_BF16 ? 2 : 4;
+    const size_t A = (size_t)T * (size_t)K;
+    const size_t ybytes = (size_t)T * (size_t)d * es;
+    const size_t wbytes = (size_t)n * (size_t)d_ff * (size_t)d * es;
+    if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, w_g, (size_t)d * n * es) ||
+        overlaps(y, ybytes, w1, wbytes) || overlaps(y, ybytes, w3, wbytes) ||
+        overlaps(y, ybytes, w2, wbytes) || overlaps(y, ybytes, workspace, L.total) ||
+        overlaps(y, ybytes, idx_out, A * 4) || overlaps(y, ybytes, gate_out, A * 4) ||
+        overlaps(y, ybytes, counts_out, (size_t)n * 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: y overlaps another argument", fn);
+    if (T == 0) return MOE_OK;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+    float* gate = gate_out ? gate_out : reinterpret_cast<float*>(ws + L.gate);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+    void* u = ws + L.u;
+    void* H = ws + L.H;
+    float* O = reinterpret_cast<float*>(ws + L.O);
+    const bool bf16 = dt == MOE_BF16;
+    const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
+
+    (void)hipGetLastError();  // clear a stale error so launch checks report our own
+    hipError_t err = moe::launch_router(bf16, block, x, w_g, T, (int)d, n, K, eps, idx, gate,
+                                        u, s);
+    if (err != hipSuccess) return hip_fail(err, "router launch");
+    err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s);
+    if (err != hipSuccess) return hip_fail(err, "permute launch");
+    const void* act = block ? u : x;
+    int splits = 1;
+    if (!bf16) {
+        err = moe::launch_gemm_f32(true, static_cast<const float*>(act), perm, K,
+                                   static_cast<const float*>(w1), static_cast<const float*>(w3),
+                                   offsets, n, (int64_t)A, (int)d, (int)d_ff,
+                                   static_cast<float*>(H), s);
+        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
+        err = moe::launch_gemm_f32(false, static_cast<const float*>(H), nullptr, K,
+                                   static_cast<const float*>(w2), nullptr, offsets, n,
+                                   (int64_t)A, (int)d_ff, (int)d, O, s);
+        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
+    } else if (plan.skinny) {
+        splits = moe::skinny_splits_used((int)d_ff, plan.down_splits);
+        err = moe::launch_gemm_bf16_skinny(true, static_cast<const uint16_t*>(act), perm, K,
+                                           static_cast<const uint16_t*>(w1),
+                                           static_cast<const uint16_t*>(w3), offsets, n,
+                                           (int64_t)A, (int)d, (int)d_ff, H, 1, s);
+        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
+        err = moe::launch_gemm_bf16_skinny(false, static_cast<const uint16_t*>(H), nullptr, K,
+                                           static_cast<const uint16_t*>(w2), nullptr, offsets,
+                                           n, (int64_t)A, (int)d_ff, (int)d, O, splits, s);
+        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
+    } else {
+        err = moe::launch_gemm_bf16_tiled(true, static_cast<const uint16_t*>(act), perm, K,
+                                          static_cast<const uint16_t*>(w1),
+                                          static_cast<const uint16_t*>(w3), offsets, n,
+                                          (int64_t)A, (int)d, (int)d_ff, H, s);
+        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
+        err = moe::launch_gemm_bf16_tiled(false, static_cast<const uint16_t*>(H), nullptr, K,
+                                          static_cast<const uint16_t*>(w2), nullptr, offsets, n,
+                                          (int64_t)A, (int)d_ff, (int)d, O, s);
+        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
+    }
+    err = moe::launch_combine(bf16, block, O, (int64_t)A, splits, inv, gate, T, K, (int)d, x, y,
+                              s);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status_t st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                           moe_dtype_t dt) {
+    if (check_sizes(T, d, d_ff, n, K, dt, true) != MOE_OK) return 0;
+    return layout(T, d, d_ff, n, K, dt).total;
+}
+
+moe_status_t moe_route(const void* x, const void* w_g, int64_t T, int64_t d, int32_t n,
+                       int32_t K, moe_dtype_t dt, int32_t* idx, float* gate, void* stream) {
+    moe_status_t st = check_sizes(T, d, 8, n, K, dt, false);
+    if (st != MOE_OK) return st;
+    if (!x || !w_g || !idx || !gate)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_route: NULL pointer argument");
+    if (!aligned(x, 16) || !aligned(w_g, 16) || !aligned(idx, 4) || !aligned(gate, 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_route: misaligned pointer argument");
+    const size_t A = (size_t)T * (size_t)K;
+    if (overlaps(idx, A * 4, gate, A * 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_route: idx and gate overlap");
+    if (T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    hipError_t err = moe::launch_router(dt == MOE_BF16, false, x, w_g, T, (int)d, n, K, 0.0f,
+                                        idx, gate, nullptr, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "router launch");
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status_t moe_permute(const int32_t* idx, int64_t T, int32_t n, int32_t K, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, void* stream) {
+    moe_status_t st = check_sizes(T, 8, 8, n, K, MOE_F32, false);
+    if (st != MOE_OK) return st;
+    if (!idx || !offsets || !perm || !inv)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_permute: NULL pointer argument");
+    if (!aligned(idx, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_permute: misaligned pointer argument");
+    if (T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    hipError_t err = moe::launch_permute(idx, T * K, n, offsets, perm, inv, nullptr,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "permute launch");
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status_t moe_forward(const void* x, const void* w_g, const void* w1, const void* w3,
+                         const void* w2, int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                         int32_t K, moe_dtype_t dt, void* y, void* workspace,
+                         size_t workspace_bytes, int32_t* idx_out, float* gate_out,
+                         int32_t* counts_out, void* stream) {
+    return layer_forward(false, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, 0.0f, y, workspace,
+                         workspace_bytes, idx_out, gate_out, counts_out, stream);
+}
+
+moe_status_t moe_block_forward(const void* x, const void* w_g, const void* w1, const void* w3,
+                               const void* w2, int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                               int32_t K, moe_dtype_t dt, float eps, void* y, void* workspace,
+                               size_t workspace_bytes, int32_t* idx_out, float* gate_out,
+                               int32_t* counts_out, void* stream) {
+    return layer_forward(true, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, eps, y, workspace,
+                         workspace_bytes, idx_out, gate_out, counts_out, stream);
+}
+
+}  // extern "C"

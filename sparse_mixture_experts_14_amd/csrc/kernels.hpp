@@ -1,0 +1,43 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router (+ optional fused pre-normalisation writing u_out).
+hipError_t launch_router(bool bf16, bool norm, const void* x, const void* wg, int64_t T,
+                         int d, int n, int K, float eps, int32_t* idx, float* gate,
+                         void* u_out, hipStream_t s);
+
+// Stable counting sort of A = T*K assignments by expert.
+hipError_t launch_permute(const int32_t* idx, int64_t A, int n, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s);
+
+// fp32 grouped GEMMs (gate/up with SiLU*mul epilogue, or down).
+hipError_t launch_gemm_f32(bool gateup, const float* A, const int32_t* perm, int K,
+                           const float* B1, const float* B3, const int32_t* offsets, int n,
+                           int64_t A_rows, int Kdim, int N, float* C, hipStream_t s);
+
+// bf16 MFMA grouped GEMMs, LDS-tiled (many rows per expert).
+hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, const int32_t* perm, int K,
+                                  const uint16_t* B1, const uint16_t* B3,
+                                  const int32_t* offsets, int n, int64_t A_rows, int Kdim,
+                                  int N, void* C, hipStream_t s);
+
+// bf16 MFMA grouped GEMMs streaming weights (few rows per expert).  The down
+// projection may split K into partial sums; skinny_splits_used() tells how
+// many splits a request of `splits` really produces.
+hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, const int32_t* perm, int K,
+                                   const uint16_t* B1, const uint16_t* B3,
+                                   const int32_t* offsets, int n, int64_t A_rows, int Kdim,
+                                   int N, void* C, int splits, hipStream_t s);
+int skinny_splits_used(int Kdim, int splits);
+
+// y = sum_k gate * (sum over S splits of O) (+ x), rounded once.
+hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int S,
+                          const int32_t* inv, const float* gate, int64_t T, int K, int d,
+                          const void* x, void* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,213 @@
+// Router: logits l = x . W_g, TopK, softmax over the kept logits.
+//
+// "Mixtral of Experts", xyznot digest, section "Method (with core equations)":
+// G(x) = Softmax(TopK(x . W_g)); TopK leaves the K largest logits and sets the
+// rest to -inf, so the softmax normalises over the K kept logits only.
+//
+// One wavefront per token.  Lane l reads the 16-byte chunks l, l+64, ... of the
+// token's row, multiplies each element with the matching row of W_g (n
+// contiguous values), and keeps n fp32 partial sums.  A butterfly reduction
+// gives every lane the same n logits (fp32, never rounded to bf16); the TopK
+// (ties to the lower index) and the softmax are then evaluated per wave.
+//
+// The pre-normalised variant (a layer of a residual stack) also accumulates
+// sum(x^2), scales the logits by rstd = 1/sqrt(mean(x^2) + eps) -- the same
+// logits as those of u = x * rstd, in fp32 -- and writes u in the storage
+// dtype for the expert GEMMs.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+template <typename TIn>
+struct Vec;
+
+template <>
+struct Vec<uint16_t> {  // bf16 storage: 8 values per 16-byte chunk
+    static constexpr int N = 8;
+    __device__ static void load(const uint16_t* p, float* f) {
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(p), f);
+    }
+    __device__ static float scalar(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+    __device__ static void store(uint16_t* p, const float* f) {
+        uint4 v;
+        v.x = pack_bf16x2(f[0], f[1]);
+        v.y = pack_bf16x2(f[2], f[3]);
+        v.z = pack_bf16x2(f[4], f[5]);
+        v.w = pack_bf16x2(f[6], f[7]);
+        *reinterpret_cast<uint4*>(p) = v;
+    }
+};
+
+template <>
+struct Vec<float> {  // fp32 storage: 4 values per 16-byte chunk
+    static constexpr int N = 4;
+    __device__ static void load(const float* p, float* f) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        f[0] = v.x;
+        f[1] = v.y;
+        f[2] = v.z;
+        f[3] = v.w;
+    }
+    __device__ static float scalar(const float* p) { return *p; }
+    __device__ static void store(float* p, const float* f) {
+        *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+};
+
+// acc[e] += xv * W_g[k][e] for e < n.  Fast path: n == NE with NE % 8 == 0
+// (bf16) or NE % 4 == 0 (fp32): the row of W_g is read as 16-byte vectors.
+template <typename TIn, int NE>
+__device__ __forceinline__ void axpy_row(const TIn* __restrict__ w, int n, float xv,
+                                         float* acc) {
+    constexpr int VN = Vec<TIn>::N;
+    if (NE % VN == 0 && n == NE) {
+#pragma unroll
+        for (int e0 = 0; e0 < NE; e0 += VN) {
+            float wf[VN];
+            Vec<TIn>::load(w + e0, wf);
+#pragma unroll
+            for (int j = 0; j < VN; ++j) acc[e0 + j] = fmaf(xv, wf[j], acc[e0 + j]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (e < n) acc[e] = fmaf(xv, Vec<TIn>::scalar(w + e), acc[e]);
+    }
+}
+
+template <typename TIn, int NE, bool NORM>
+__global__ __launch_bounds__(256) void router_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ wg, int64_t T, int d, int n,
+    int K, float eps, int32_t* __restrict__ idx, float* __restrict__ gate,
+    TIn* __restrict__ u_out) {
+    constexpr int VN = Vec<TIn>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    if (t >= T) return;
+    const TIn* __restrict__ xr = x + t * (int64_t)d;
+
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
+    float ss = 0.0f;
+
+    // d is a multiple of 8, so every chunk is either whole or absent.
+    for (int k0 = lane * VN; k0 < d; k0 += kWave * VN) {
+        float xv[VN];
+        Vec<TIn>::load(xr + k0, xv);
+#pragma unroll
+        for (int j = 0; j < VN; ++j) {
+            if (NORM) ss = fmaf(xv[j], xv[j], ss);
+            axpy_row<TIn, NE>(wg + (int64_t)(k0 + j) * n, n, xv[j], acc);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = wave_sum(acc[e]);
+    float rstd = 1.0f;
+    if (NORM) {
+        ss = wave_sum(ss);
+        rstd = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] *= rstd;
+    }
+
+    if (lane == 0) {
+        // TopK: K rounds of "largest logit not yet taken"; a later expert
+        // needs a strictly larger logit, so ties go to the lower index.
+        uint64_t taken = 0;
+        int sel[8];
+        float val[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < K) {
+                int best = -1;
+                float bv = 0.0f;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    if (e < n && !((taken >> e) & 1ull)) {
+                        if (best < 0 || acc[e] > bv) {
+                            best = e;
+                            bv = acc[e];
+                        }
+                    }
+                }
+                taken |= 1ull << best;
+                sel[j] = best;
+                val[j] = bv;
+            }
+        }
+        // Softmax over the kept logits; val[0] is the largest.
+        float g[8];
+        float z = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < K) {
+                g[j] = expf(val[j] - val[0]);
+                z += g[j];
+            }
+        }
+        const float rz = 1.0f / z;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < K) {
+                idx[t * K + j] = sel[j];
+                gate[t * K + j] = g[j] * rz;
+            }
+        }
+    }
+
+    if (NORM) {
+        TIn* __restrict__ ur = u_out + t * (int64_t)d;
+        for (int k0 = lane * VN; k0 < d; k0 += kWave * VN) {
+            float xv[VN];
+            Vec<TIn>::load(xr + k0, xv);
+#pragma unroll
+            for (int j = 0; j < VN; ++j) xv[j] *= rstd;
+            Vec<TIn>::store(ur + k0, xv);
+        }
+    }
+}
+
+template <typename TIn, bool NORM>
+hipError_t launch_router_t(const void* x, const void* wg, int64_t T, int d, int n, int K,
+                           float eps, int32_t* idx, float* gate, void* u_out,
+                           hipStream_t s) {
+    const int wpb = 4;
+    const dim3 grid((unsigned)((T + wpb - 1) / wpb));
+    const dim3 block(wpb * kWave);
+    const TIn* xp = static_cast<const TIn*>(x);
+    const TIn* wp = static_cast<const TIn*>(wg);
+    TIn* up = static_cast<TIn*>(u_out);
+    if (n <= 8)
+        hipLaunchKernelGGL((router_kernel<TIn, 8, NORM>), grid, block, 0, s, xp, wp, T, d,
+                           n, K, eps, idx, gate, up);
+    else if (n <= 16)
+        hipLaunchKernelGGL((router_kernel<TIn, 16, NORM>), grid, block, 0, s, xp, wp, T,
+                           d, n, K, eps, idx, gate, up);
+    else if (n <= 32)
+        hipLaunchKernelGGL((router_kernel<TIn, 32, NORM>), grid, block, 0, s, xp, wp, T,
+                           d, n, K, eps, idx, gate, up);
+    else
+        hipLaunchKernelGGL((router_kernel<TIn, 64, NORM>), grid, block, 0, s, xp, wp, T,
+                           d, n, K, eps, idx, gate, up);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router(bool bf16, bool norm, const void* x, const void* wg, int64_t T,
+                         int d, int n, int K, float eps, int32_t* idx, float* gate,
+                         void* u_out, hipStream_t s) {
+    if (bf16)
+        return norm ? launch_router_t<uint16_t, true>(x, wg, T, d, n, K, eps, idx, gate,
+                                                      u_out, s)
+                    : launch_router_t<uint16_t, false>(x, wg, T, d, n, K, eps, idx, gate,
+                                                       u_out, s);
+    return norm ? launch_router_t<float, true>(x, wg, T, d, n, K, eps, idx, gate, u_out, s)
+                : launch_router_t<float, false>(x, wg, T, d, n, K, eps, idx, gate, u_out,
+                                                s);
+}
+
+}  // namespace moe

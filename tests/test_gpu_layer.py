@@ -1,0 +1,115 @@
+"""GPU parity of the whole layer (moe_forward / moe_block_forward through the
+C ABI) against the fp64 oracle on small seeded inputs: several tiles with
+ragged tails in every dimension, both bf16 GEMM paths, fp32, and the
+degenerate cases of the method (one token, no tokens, empty experts, every
+token on one expert, exact ties, K = 1, n = 1, K = n, large n)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_mixture_experts_14_amd as moe
+from tests import parity as P
+from tests.gpu_common import check_layer, forced_path, small_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32_workload():
+    from sparse_mixture_experts_14_amd import workloads as W
+    L = W.make_layer(W.WORKLOADS["tiny"], device="cuda")
+    rep, _ = check_layer(L, 2, label="tiny")
+    assert rep["rel_l2"] <= 1e-5
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("T,d,d_ff", [(300, 256, 328), (77, 200, 256), (513, 128, 192)])
+def test_bf16_ragged(path, T, d, d_ff):
+    L = small_layer(T, d, d_ff, 8, 2, seed=T)
+    check_layer(L, 2, path=path, label=f"ragged-{path}")
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_fp32_ragged(path):
+    L = small_layer(150, 136, 200, 8, 2, dtype="f32", seed=3)
+    check_layer(L, 2, path=path, label="f32-ragged")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 17])
+def test_few_tokens_leave_experts_empty(T):
+    L = small_layer(T, 256, 320, 8, 2, seed=100 + T)
+    rep, _ = check_layer(L, 2, label=f"T={T}")
+
+
+def test_zero_tokens():
+    L = small_layer(4, 64, 64, 8, 2)
+    x = L["x"][:0]
+    y, idx, gate, counts = moe.forward(x, L["Wg"], L["W1"], L["W3"], L["W2"], 2)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+
+
+@pytest.mark.parametrize("K", [1, 2])
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_every_token_on_one_expert(K, path):
+    L = small_layer(200, 128, 256, 8, K, seed=7)
+    x = L["x"].float().abs()
+    L["x"] = x.to(torch.bfloat16)
+    wg = L["Wg"].float()
+    wg[:, 5] = 4.0 / math.sqrt(128)
+    L["Wg"] = wg.to(torch.bfloat16)
+    rep, _ = check_layer(L, K, path=path, label="one-expert")
+
+
+def test_exact_ties_go_to_lower_index():
+    L = small_layer(64, 128, 128, 8, 2, seed=9)
+    wg = L["Wg"].clone()
+    wg[:, 6] = wg[:, 1]   # experts 1 and 6 always tie
+    wg[:, 4] = wg[:, 3]   # experts 3 and 4 always tie
+    L["Wg"] = wg
+    rep, _ = check_layer(L, 2, label="ties")
+    idx, _ = moe.route(L["x"], L["Wg"], 2)
+    idx = P.to_np(idx)
+    # the higher twin is only ever chosen together with its lower twin
+    for lo, hi in [(1, 6), (3, 4)]:
+        has_hi = (idx == hi).any(1)
+        assert (idx[has_hi] == lo).any(1).all()
+        slot_lo = np.argmax(idx[has_hi] == lo, 1)
+        slot_hi = np.argmax(idx[has_hi] == hi, 1)
+        assert (slot_lo < slot_hi).all()
+
+
+def test_zero_tokens_route_to_first_two():
+    L = small_layer(32, 128, 128, 8, 2, seed=11)
+    L["x"] = torch.zeros_like(L["x"])
+    idx, gate = moe.route(L["x"], L["Wg"], 2)
+    assert (P.to_np(idx) == [0, 1]).all() and (P.to_np(gate) == 0.5).all()
+    rep, y = check_layer(L, 2, label="x=0")
+    assert torch.count_nonzero(y) == 0
+
+
+@pytest.mark.parametrize("n,K", [(1, 1), (4, 4), (13, 3), (64, 8), (16, 1), (8, 8)])
+def test_other_expert_counts(n, K):
+    L = small_layer(96, 128, 136, n, K, seed=n * 10 + K)
+    check_layer(L, K, label=f"n={n},K={K}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_layer_small(dtype):
+    L = small_layer(100, 256, 264, 8, 2, dtype=dtype, seed=21)
+    L["x"] = (L["x"].float() * 3.0).to(L["x"].dtype)
+    check_layer(L, 2, block=True, eps=1e-5, label="block")
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_deterministic_and_permutation_equivariant(path):
+    L = small_layer(257, 256, 256, 8, 2, seed=31)
+    with forced_path(path):
+        y1 = moe.forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], 2)[0]
+        y2 = moe.forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], 2)[0]
+        p = torch.randperm(257, generator=torch.Generator().manual_seed(0)).cuda()
+        yp = moe.forward(L["x"][p].contiguous(), L["Wg"], L["W1"], L["W3"], L["W2"], 2)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(yp, y1[p])
