@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer (top-2 of 8 SwiGLU experts, d = 4096) on one
+MI355X, with the roofline of its dominant kernel and the fp64 oracle's CPU
+throughput beside it.
+
+One step = one call of the whole layer (router, permutation, gate/up GEMM,
+down GEMM, combine) on the workload's synthetic batch, inputs resident in HBM.
+Default workload: decode (T = 16 tokens, d = 4096, d_ff = 14336, n = 8, K = 2,
+bf16), bound by reading the touched experts' weights.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skew|stack|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (top-2 of 8 SwiGLU, d=4096) + % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_14_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvent:
+    """A raw hipEvent_t (the library records it on the stream it launches
+    on; torch.cuda.Event only knows about records made through torch)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._c = ctypes
+        self.handle = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = self._c.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._c.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.handle:
+            HipEvent._hip.hipEventDestroy(self.handle)
+
+
+def kernel_source_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_kernel(w, skinny: bool):
+    """The stage that moves the most bytes (decode) or does the most flops
+    (the others): the gate/up grouped GEMM in every workload."""
+    src = ["gemm_skinny.hip" if skinny else "gemm_bf16.hip", "common.hpp"]
+    if w.dtype == "f32":
+        src = ["gemm_f32.hip", "common.hpp"]
+    return "gate_up", src
+
+
+def algorithmic_work(w, counts):
+    """Per launch of the gate/up kernel: bytes it must move (decode) and flops
+    it must do.  Units: a touched expert's W1 and W3 (2 * d_ff * d elements),
+    plus the gathered token rows read and the hidden rows written."""
+    es = 2 if w.dtype == "bf16" else 4
+    A = w.T * w.K
+    touched = int(sum(1 for c in counts if c > 0))
+    wbytes = touched * 2 * w.d_ff * w.d * es
+    act = A * w.d * es + A * w.d_ff * es
+    flops = 4.0 * A * w.d * w.d_ff
+    return {"touched_experts": touched, "bytes": wbytes + act, "flops": flops}
+
+
+def cpu_baseline(w, L, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload's
+    tokens (timing each oracle call; repeats until ~budget_s)."""
+    import numpy as np
+
+    import oracle
+    H = {k: oracle._f32(v) for k, v in L.items()}
+    eps = w.eps
+    def run(rows):
+        if eps is not None:
+            return oracle.block_forward(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], w.K, eps,
+                                        rows=rows)
+        return oracle.forward(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], w.K, rows=rows)
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(w.T, min(w.T, 16), replace=False))
+    t0 = time.perf_counter()
+    run(probe)
+    per_tok = (time.perf_counter() - t0) / len(probe)
+    n_tok = max(1, int(budget_s / max(per_tok, 1e-9)))
+    reps, tokens, elapsed = 0, 0, 0.0
+    while elapsed < budget_s * 0.5 or reps == 0:
+        rows = np.sort(rng.choice(w.T, min(w.T, n_tok), replace=False))
+        t0 = time.perf_counter()
+        run(rows)
+        elapsed += time.perf_counter() - t0
+        tokens += len(rows)
+        reps += 1
+    if tokens == w.T * reps:
+        sample = f"all {w.T} tokens of the workload x{reps}"
+    else:
+        sample = f"{tokens} tokens drawn from the workload's {w.T} ({reps} oracle call(s))"
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def traffic_for(workload: str, src_sha: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when there is none or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != src_sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "skew", "stack"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer is built and timed on a single MI355X; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mixture_experts_14_amd as moe
+    from sparse_mixture_experts_14_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.load()
+    log(f"[bench] workload={w.name} T={w.T} building inputs on {dev}")
+    if w.name == "stack":
+        layers = [W.make_stack_layer(w, l, device=dev) for l in range(w.layers)]
+        x0 = W.make_stack_input(w, device=dev)
+    else:
+        L = W.make_layer(w, device=dev)
+        layers = [L]
+        x0 = L["x"]
+    lay = moe.Layer(w.T, w.d, w.d_ff, w.n, w.K, w.torch_dtype, dev)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+
+    def step(stage_ev=None):
+        x = x0
+        for i, P in enumerate(layers):
+            y = bufs[i % 2]
+            if stage_ev is not None:
+                moe._lib.set_stage_events_raw("gate_up", stage_ev[i][0].handle.value,
+                                              stage_ev[i][1].handle.value)
+            if w.eps is not None:
+                lay.block_forward(x, P["Wg"], P["W1"], P["W3"], P["W2"], w.eps, out=y)
+            else:
+                lay.forward(x, P["Wg"], P["W1"], P["W3"], P["W2"], out=y)
+            x = y
+        return x
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    nl = len(layers)
+    kev = [[(HipEvent(), HipEvent()) for _ in range(nl)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(kev[s])
+    end.record()
+    torch.cuda.synchronize()
+    moe._lib.set_stage_events_raw("gate_up")
+    ms = start.elapsed_time(end) / args.steps
+    k_ms = [a.elapsed_ms(b) for st in kev for (a, b) in st]
+    k_avg = sum(k_ms) / len(k_ms)
+    counts = lay.counts.cpu().tolist()
+    log(f"[bench] {ms:.4f} ms/step, gate/up kernel {k_avg:.4f} ms avg, counts {counts}")
+
+    skinny = w.dtype == "bf16" and w.T * w.K <= 16 * w.n
+    kname, ksrc = dominant_kernel(w, skinny)
+    sha = kernel_source_sha(ksrc)
+    work = algorithmic_work(w, counts)
+    if w.name == "decode":
+        ach = work["bytes"] / (k_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+        ach = work["flops"] / (k_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(ach, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    roof["traffic"] = traffic_for(w.name, sha)
+    roof["kernel"] = f"{kname} ({'skinny' if skinny else 'tiled'} grouped GEMM)"
+    roof["kernel_ms"] = round(k_avg, 5)
+    roof["algorithmic_bytes"] = work["bytes"]
+    roof["algorithmic_flops"] = work["flops"]
+    roof["touched_experts"] = work["touched_experts"]
+    roof["source_sha"] = sha
+
+    tokens = w.T  # tokens through the whole step (all layers of the stack)
+    value = tokens / (ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "n": w.n, "K": w.K,
+                   "layers": w.layers, "dtype": w.dtype},
+        "roofline": roof,
+    }
+    # whole-step rate over the touched weights, for context
+    if w.name in ("decode",):
+        step_bytes = work["touched_experts"] * 3 * w.d_ff * w.d * 2
+        out["step_hbm_gbs"] = round(step_bytes / (ms * 1e-3) / 1e9, 1)
+    else:
+        out["step_tflops"] = round(6.0 * w.T * w.K * w.d * w.d_ff * nl / (ms * 1e-3) / 1e12, 1)
+    if args.cpu_budget > 0:
+        log("[bench] timing the fp64 oracle on the host")
+        Ls = dict(layers[0])
+        Ls["x"] = x0
+        cb = cpu_baseline(w, Ls, args.cpu_budget)
+        if nl > 1:  # tokens through the whole stack: one layer's rate / layers
+            cb["value"] /= nl
+            cb["sample"] += f" through layer 0 only; rate divided by {nl} layers"
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -75,6 +75,15 @@ typedef enum moe_dtype {
     MOE_BF16 = 1  /* bf16 storage, fp32 accumulation */
 } moe_dtype_t;
 
+/* Stages of moe_forward / moe_block_forward, in launch order. */
+typedef enum moe_stage {
+    MOE_STAGE_ROUTER = 0,   /* logits, TopK, softmax (and RMSNorm in the block layer) */
+    MOE_STAGE_PERMUTE = 1,  /* per-expert grouping of the assignments */
+    MOE_STAGE_GATE_UP = 2,  /* H = SiLU(u W1^T) * (u W3^T), grouped by expert */
+    MOE_STAGE_DOWN = 3,     /* O = H W2^T, grouped by expert */
+    MOE_STAGE_COMBINE = 4   /* y = sum_k gate * O (+ x), back in token order */
+} moe_stage_t;
+
 /* Version of this ABI (MOE_ABI_VERSION of the library that was built). */
 int32_t moe_abi_version(void);
 
@@ -130,6 +139,14 @@ moe_status_t moe_block_forward(const void* x, const void* w_g, const void* w1,
                                size_t workspace_bytes, int32_t* idx_out,
                                float* gate_out, int32_t* counts_out,
                                void* stream);
+
+/* Timing hook (for profilers and benchmarks, not part of the layer): in later
+ * moe_forward / moe_block_forward calls made by this thread, record
+ * start_event on the call's stream right before `stage` is launched and
+ * end_event right after it.  Both are caller-owned hipEvent_t handles that
+ * must stay valid while set; NULL, NULL clears the hook.  Returns
+ * MOE_ERR_INVALID_ARGUMENT for an unknown stage or a single NULL. */
+moe_status_t moe_set_stage_events(int32_t stage, void* start_event, void* end_event);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t status);

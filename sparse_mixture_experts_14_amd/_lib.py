@@ -24,7 +24,9 @@ MOE_F32 = 0
 MOE_BF16 = 1
 
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
-           "moe_forward", "moe_block_forward", "moe_status_string", "moe_last_error")
+           "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
+           "moe_last_error")
+STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4}
 
 
 class MoeError(RuntimeError):
@@ -62,6 +64,8 @@ def load(path: str | None = None):
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, V, V, SZ,
                                 V, V, V, V]
+    lib.moe_set_stage_events.restype = ctypes.c_int
+    lib.moe_set_stage_events.argtypes = [I32, V, V]
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, F,
                                       V, V, SZ, V, V, V, V]
@@ -98,6 +102,12 @@ def _ptr(t):
 
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def set_stage_events_raw(stage: str, start: int | None = None, end: int | None = None):
+    """Record the hipEvent_t handles (start, end) around `stage` in later layer
+    calls on this thread; no handles clears the hook."""
+    _check(load().moe_set_stage_events(STAGES[stage], start, end), "moe_set_stage_events")
 
 
 def workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int, dtype: torch.dtype) -> int:

@@ -19,6 +19,12 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+// Per-thread timing hooks (moe_set_stage_events): events recorded on the
+// call's stream right before and right after one stage's kernel launch.
+constexpr int kStages = 5;
+thread_local hipEvent_t g_ev_start[kStages] = {};
+thread_local hipEvent_t g_ev_end[kStages] = {};
+
 moe_status_t fail(moe_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 moe_status_t fail(moe_status_t st, const char* fmt, ...) {
     va_list ap;
@@ -133,6 +139,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     const void* ptrs[] = {x, w_g, w1, w3, w2, y};
     const char* names[] = {"x", "w_g", "w1", "w3", "w2", "y"};
     for (int i = 0; i < 6; ++i) {
+        // x and y hold T rows: with T = 0 they may be NULL
+        if (!ptrs[i] && T == 0 && (i == 0 || i == 5)) continue;
         if (!ptrs[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
         if (!aligned(ptrs[i], 16))
             return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
@@ -177,47 +185,58 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
 
     (void)hipGetLastError();  // clear a stale error so launch checks report our own
-    hipError_t err = moe::launch_router(bf16, block, x, w_g, T, (int)d, n, K, eps, idx, gate,
-                                        u, s);
+    hipError_t err = hipSuccess;
+    auto mark = [&](hipEvent_t ev) {
+        if (ev && err == hipSuccess) err = hipEventRecord(ev, s);
+    };
+    mark(g_ev_start[MOE_STAGE_ROUTER]);
+    if (err == hipSuccess)
+        err = moe::launch_router(bf16, block, x, w_g, T, (int)d, n, K, eps, idx, gate, u, s);
+    mark(g_ev_end[MOE_STAGE_ROUTER]);
     if (err != hipSuccess) return hip_fail(err, "router launch");
-    err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s);
+    mark(g_ev_start[MOE_STAGE_PERMUTE]);
+    if (err == hipSuccess)
+        err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s);
+    mark(g_ev_end[MOE_STAGE_PERMUTE]);
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     const void* act = block ? u : x;
     int splits = 1;
-    if (!bf16) {
-        err = moe::launch_gemm_f32(true, static_cast<const float*>(act), perm, K,
-                                   static_cast<const float*>(w1), static_cast<const float*>(w3),
-                                   offsets, n, (int64_t)A, (int)d, (int)d_ff,
-                                   static_cast<float*>(H), s);
-        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
-        err = moe::launch_gemm_f32(false, static_cast<const float*>(H), nullptr, K,
-                                   static_cast<const float*>(w2), nullptr, offsets, n,
-                                   (int64_t)A, (int)d_ff, (int)d, O, s);
-        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
-    } else if (plan.skinny) {
-        splits = moe::skinny_splits_used((int)d_ff, plan.down_splits);
-        err = moe::launch_gemm_bf16_skinny(true, static_cast<const uint16_t*>(act), perm, K,
-                                           static_cast<const uint16_t*>(w1),
-                                           static_cast<const uint16_t*>(w3), offsets, n,
-                                           (int64_t)A, (int)d, (int)d_ff, H, 1, s);
-        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
-        err = moe::launch_gemm_bf16_skinny(false, static_cast<const uint16_t*>(H), nullptr, K,
-                                           static_cast<const uint16_t*>(w2), nullptr, offsets,
-                                           n, (int64_t)A, (int)d_ff, (int)d, O, splits, s);
-        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
-    } else {
-        err = moe::launch_gemm_bf16_tiled(true, static_cast<const uint16_t*>(act), perm, K,
-                                          static_cast<const uint16_t*>(w1),
-                                          static_cast<const uint16_t*>(w3), offsets, n,
-                                          (int64_t)A, (int)d, (int)d_ff, H, s);
-        if (err != hipSuccess) return hip_fail(err, "gate/up GEMM launch");
-        err = moe::launch_gemm_bf16_tiled(false, static_cast<const uint16_t*>(H), nullptr, K,
-                                          static_cast<const uint16_t*>(w2), nullptr, offsets, n,
-                                          (int64_t)A, (int)d_ff, (int)d, O, s);
-        if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
+    if (bf16 && plan.skinny) splits = moe::skinny_splits_used((int)d_ff, plan.down_splits);
+    for (int stage = MOE_STAGE_GATE_UP; stage <= MOE_STAGE_DOWN; ++stage) {
+        const bool gu = stage == MOE_STAGE_GATE_UP;
+        const void* a_in = gu ? act : H;
+        const void* b1 = gu ? w1 : w2;
+        const void* b3 = gu ? w3 : nullptr;
+        void* c_out = gu ? H : static_cast<void*>(O);
+        const int kdim = (int)(gu ? d : d_ff), ndim = (int)(gu ? d_ff : d);
+        const int32_t* pm = gu ? perm : nullptr;
+        mark(g_ev_start[stage]);
+        if (err == hipSuccess) {
+            if (!bf16)
+                err = moe::launch_gemm_f32(gu, static_cast<const float*>(a_in), pm, K,
+                                           static_cast<const float*>(b1),
+                                           static_cast<const float*>(b3), offsets, n,
+                                           (int64_t)A, kdim, ndim, static_cast<float*>(c_out), s);
+            else if (plan.skinny)
+                err = moe::launch_gemm_bf16_skinny(gu, static_cast<const uint16_t*>(a_in), pm, K,
+                                                   static_cast<const uint16_t*>(b1),
+                                                   static_cast<const uint16_t*>(b3), offsets, n,
+                                                   (int64_t)A, kdim, ndim, c_out,
+                                                   gu ? 1 : splits, s);
+            else
+                err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in), pm, K,
+                                                  static_cast<const uint16_t*>(b1),
+                                                  static_cast<const uint16_t*>(b3), offsets, n,
+                                                  (int64_t)A, kdim, ndim, c_out, s);
+        }
+        mark(g_ev_end[stage]);
+        if (err != hipSuccess) return hip_fail(err, gu ? "gate/up GEMM launch" : "down GEMM launch");
     }
-    err = moe::launch_combine(bf16, block, O, (int64_t)A, splits, inv, gate, T, K, (int)d, x, y,
-                              s);
+    mark(g_ev_start[MOE_STAGE_COMBINE]);
+    if (err == hipSuccess)
+        err = moe::launch_combine(bf16, block, O, (int64_t)A, splits, inv, gate, T, K, (int)d, x,
+                                  y, s);
+    mark(g_ev_end[MOE_STAGE_COMBINE]);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
     g_last_error[0] = '\0';
     return MOE_OK;
@@ -282,6 +301,16 @@ moe_status_t moe_permute(const int32_t* idx, int64_t T, int32_t n, int32_t K, in
                                          reinterpret_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status_t moe_set_stage_events(int32_t stage, void* start_event, void* end_event) {
+    if (stage < 0 || stage >= kStages)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_set_stage_events: stage %d", stage);
+    if ((start_event == nullptr) != (end_event == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_set_stage_events: give both events or none");
+    g_ev_start[stage] = static_cast<hipEvent_t>(start_event);
+    g_ev_end[stage] = static_cast<hipEvent_t>(end_event);
     return MOE_OK;
 }
 
