@@ -49,9 +49,44 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 // projection uses.  Depends on sizes only (so the workspace bound holds); the
 // environment variable MOE_GEMM_PATH=tiled|skinny forces a bf16 path (a
 // testing and tuning knob).
-// K splits of the skinny down projection: more workgroups when there are
-// few rows (decode), none otherwise.
-int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 4 : 1; }
+// Upper bound of the K splits of the skinny down projection (partial sums in
+// the workspace): splits only pay off with few rows.
+int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 1; }
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+// K splits of the skinny down projection: the split count in [1, max_splits]
+// whose item count (all n experts touched) spreads most evenly over the
+// persistent waves; ties go to fewer splits.
+int choose_down_splits(int32_t n, int64_t d, int64_t d_ff, int max_splits, int waves) {
+    const int64_t groups = (d + 15) / 16;  // 16 output columns per item
+    int best = 1;
+    double best_eff = -1.0;
+    for (int s = 1; s <= max_splits; ++s) {
+        if (moe::skinny_splits_used((int)d_ff, s) != s) continue;
+        const int64_t items = (int64_t)n * groups * s;
+        const int64_t rounds = (items + waves - 1) / waves;
+        const double eff = (double)items / (double)(rounds * waves);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = s;
+        }
+    }
+    return best;
+}
 
 struct Plan {
     bool skinny;
@@ -68,10 +103,11 @@ Plan choose_plan(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_d
         if (!strcmp(f, "tiled")) p.skinny = false;
         if (!strcmp(f, "skinny")) p.skinny = true;
     }
+    if (!moe::skinny_fits(T, A, d, d_ff, 1) ||
+        !moe::skinny_fits(A, A, d_ff, d, requested_down_splits(T, K)))
+        p.skinny = false;
     // splits requested; the launcher may use fewer (never more) when d_ff is short
     if (p.skinny) p.down_splits = requested_down_splits(T, K);
-    (void)d;
-    (void)d_ff;
     return p;
 }
 
@@ -201,7 +237,10 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     const void* act = block ? u : x;
     int splits = 1;
-    if (bf16 && plan.skinny) splits = moe::skinny_splits_used((int)d_ff, plan.down_splits);
+    const int cus = device_cus();
+    if (bf16 && plan.skinny)
+        splits = choose_down_splits(n, d, d_ff, plan.down_splits,
+                                    cus * moe::skinny_waves_per_cu());
     for (int stage = MOE_STAGE_GATE_UP; stage <= MOE_STAGE_DOWN; ++stage) {
         const bool gu = stage == MOE_STAGE_GATE_UP;
         const void* a_in = gu ? act : H;
@@ -218,11 +257,12 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                            static_cast<const float*>(b3), offsets, n,
                                            (int64_t)A, kdim, ndim, static_cast<float*>(c_out), s);
             else if (plan.skinny)
-                err = moe::launch_gemm_bf16_skinny(gu, static_cast<const uint16_t*>(a_in), pm, K,
+                err = moe::launch_gemm_bf16_skinny(gu, static_cast<const uint16_t*>(a_in),
+                                                   gu ? T : (int64_t)A, pm, K,
                                                    static_cast<const uint16_t*>(b1),
                                                    static_cast<const uint16_t*>(b3), offsets, n,
                                                    (int64_t)A, kdim, ndim, c_out,
-                                                   gu ? 1 : splits, s);
+                                                   gu ? 1 : splits, cus, s);
             else
                 err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in), pm, K,
                                                   static_cast<const uint16_t*>(b1),

@@ -38,7 +38,13 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
     f[7] = __uint_as_float(v.w & 0xffff0000u);
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 

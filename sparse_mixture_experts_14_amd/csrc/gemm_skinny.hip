@@ -3,177 +3,334 @@
 // Same products as the tiled kernels (xyznot digest of "Mixtral of Experts",
 // "Method" section: SwiGLU_e(u) = W2_e (SiLU(W1_e u) (*) W3_e u)), but with a
 // handful of tokens per expert the layer is bound by reading the touched
-// experts' weights from HBM once.  Each wavefront streams 16-column slices of
-// the weight matrices straight from global memory into MFMA B operands
-// (v_mfma_f32_16x16x32_bf16; the token rows, zero-padded to 16, are the A
-// operand and come from L2), so no LDS round trip sits on the weight path.
+// experts' weights from HBM once; everything here serves that stream.
 //
-// K permutation: in one step a lane loads 4 consecutive 16-byte chunks (64
-// contiguous bytes) of its weight row; MFMA sub-step c uses chunk c.  Lane
-// group g = lane/16 covers k in [k0 + 32g, k0 + 32g + 32), the A operand is
-// loaded with the same k map, so the products are unchanged while each row
-// is read in 64-byte runs.  The next step's loads are issued before the
-// current step's MFMAs (register double buffering).
-//
-// An expert with no rows exits at once and reads no weights (the pages: an
-// expert whose gate is 0 need not be computed).  Down projection: blockIdx.z
-// splits K; split s writes its partial sums to O + s * A_rows * N and the
-// combine stage adds the splits in order (deterministic, no atomics).
+// * Work split.  An item is a 16-row slice of weights (16 output columns)
+//   over one K range: gate/up -- rows f..f+15 of W1_e, then the same rows of
+//   W3_e (the SiLU*mul epilogue needs both); down -- rows c..c+15 of W2_e over
+//   one of S K-splits (partial sums go to O + s * A_rows * N and the combine
+//   stage adds the S splits in order).  Items of experts with no rows do not
+//   exist (an expert whose gate is 0 is never read).  The grid is
+//   persistent: one workgroup of W waves per CU (its LDS keeps a second one
+//   off the CU) and wave g takes items g, g + NW, ...; the host picks S so
+//   that items divide evenly over the waves.
+// * Weight loads.  HBM streams best in long runs per row, so every load
+//   instruction reads 1 KB of one weight row (lane l: elements 8l..8l+7 of a
+//   512-element step), non-temporal, into registers; the wave then writes the
+//   16 rows x 512 elements to its own 16 KB LDS tile and reads MFMA A
+//   fragments (v_mfma_f32_16x16x32_bf16, weights as the 16-row operand) back
+//   out of it.  The LDS chunk index is XOR-swizzled by the row, so both the
+//   row-wise writes and the fragment reads hit distinct banks.  Token rows
+//   (the B operand, <= 16 per pass, padding lanes read nothing) come from L2
+//   straight in fragment layout.
+// * K map.  Fragment c of a step takes chunk 4c + g (g = lane/16) for both
+//   operands, so weights and tokens agree on k and the products are unchanged.
+// * Buffer instructions.  Loads and stores go through buffer resources (one
+//   per expert matrix, per activation array, per output), so offsets are
+//   32-bit and a store at an out-of-range offset is dropped by the hardware.
+//   The epilogue store is issued on every step with no branch (only its
+//   offset decides whether it lands), which keeps the instruction stream
+//   fixed so that the compiler counts outstanding loads exactly.
+// * Tables.  At start the workgroup copies the touched experts' row ranges
+//   and the activation row of every expert-ordered row into LDS; the step
+//   loop reads only LDS besides the streams, so no table lookup drains the
+//   loads in flight.
+// * Pipeline, per step s: MFMAs of step s from LDS; write step s+1's rows
+//   (loaded one step earlier) into LDS; load step s+1's token fragments;
+//   load step s+2's weight rows; store.  One step of weights stays in flight
+//   per wave while it computes.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int KSTEP = 128;  // k per step: 4 lane groups x 32
 
-template <bool GATEUP, int NT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
+constexpr int KSTEP = 512;         // k per step: 64 lanes x 8 elements of one row
+constexpr int WAVES = 7;           // waves per workgroup (= per CU)
+constexpr int MAX_ROWS = 2048;     // row-source table in LDS (the host keeps A <= this)
+constexpr int TILE_U4 = 16 * 64;   // one wave's LDS tile: 16 rows x 64 chunks of 16 bytes
+
+struct Shape {
+    int Kdim, N, nsplit, ksplit, tiles, groups, steps, total_items, NW;
+};
+
+struct Tables {  // per-workgroup copies in LDS, so the step loop never waits on memory
+    int t_expert[64], t_start[64], t_end[64];
+    int src[MAX_ROWS];  // activation row feeding expert-ordered row p
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Everything an item implies (recomputed only when the cursor changes item).
+struct Where {
+    int expert, end, col0, split, kbeg, kend;
+};
+
+// A cursor over the wave's flat step sequence: items gw, gw + NW, ...; each
+// item in 16-row passes; each pass streams its weight slices (tiles) one
+// after the other, each in `steps` K steps.  Plain scalars only.
+struct Cursor {
+    int item, row0, tile, step;
+    bool valid;
+    Where w;
+};
+
+__device__ __forceinline__ Where where(const Tables& tb, const Shape& S, int item) {
+    Where w;
+    const int per_expert = S.groups * S.nsplit;
+    const int ti = item / per_expert;
+    const int rem = item - ti * per_expert;
+    const int grp = rem / S.nsplit;
+    w.split = rem - grp * S.nsplit;
+    w.expert = uni(tb.t_expert[ti]);
+    w.end = uni(tb.t_end[ti]);
+    w.col0 = grp * 16;
+    w.kbeg = w.split * S.ksplit;
+    w.kend = min(S.Kdim, w.kbeg + S.ksplit);
+    return w;
+}
+
+__device__ __forceinline__ Cursor start_cursor(const Tables& tb, const Shape& S, int item) {
+    Cursor c;
+    c.item = item;
+    c.row0 = uni(tb.t_start[item / (S.groups * S.nsplit)]);
+    c.tile = 0;
+    c.step = 0;
+    c.valid = true;
+    c.w = where(tb, S, item);
+    return c;
+}
+
+// One step on: next K step, next tile, next 16-row pass, or the wave's next
+// item.  Past the end the cursor stays on its last step with valid = false.
+__device__ __forceinline__ void step_on(const Tables& tb, const Shape& S, Cursor& c) {
+    if (!c.valid) return;
+    if (++c.step < S.steps) return;
+    c.step = 0;
+    if (c.tile + 1 < S.tiles) {
+        ++c.tile;
+    } else if (c.row0 + 16 < c.w.end) {
+        c.tile = 0;
+        c.row0 += 16;
+    } else if (c.item + S.NW < S.total_items) {
+        c = start_cursor(tb, S, c.item + S.NW);
+    } else {
+        c.valid = false;
+        c.step = S.steps - 1;
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every range: load 0, store dropped
+constexpr int NT_AUX = 2;              // non-temporal cache policy
+
+// LDS position (in 16-byte units) of chunk q of tile row r.
+__device__ __forceinline__ int lds_pos(int r, int q) { return r * 64 + (q ^ r); }
+
+template <bool GATEUP, bool KTAIL>
+__global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm, int K,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
-    const int32_t* __restrict__ offsets, int Kdim, int N, void* __restrict__ Cout,
-    int ksplit, int64_t A_rows) {
-    constexpr int CW = GATEUP ? NT / 2 * 16 : NT * 16;  // output columns per wave
-    const int e = blockIdx.y;
-    const int start = offsets[e];
-    const int M = offsets[e + 1] - start;
-    if (M <= 0) return;
+    const int32_t* __restrict__ offsets, int n, int Kdim, int N, void* __restrict__ Cout,
+    int64_t A_rows, int64_t A_src_rows, int nsplit, int ksplit) {
+    __shared__ Tables tb;
+    __shared__ int s_touched;
+    __shared__ u32x4_t tiles_lds[WAVES * TILE_U4];
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    const int col0 = (blockIdx.x * (blockDim.x / kWave) + w) * CW;
-    if (col0 >= N) return;
-    const int kbeg = blockIdx.z * ksplit;
-    const int kend = min(Kdim, kbeg + ksplit);
+    const int wv = threadIdx.x / kWave;
+    // the wave index is uniform across the wave: keep the cursors in SGPRs
+    const int gw = uni(blockIdx.x * WAVES + wv);
+    const int j16 = lane & 15, g = lane >> 4;
+    u32x4_t* tile = tiles_lds + wv * TILE_U4;
 
-    const int j = lane & 15, g = lane >> 4;
-    const uint16_t* b_ptr[NT];
-    bool b_ok[NT];
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int e = 0; e < n; ++e) {
+            const int s0 = offsets[e], s1 = offsets[e + 1];
+            if (s1 > s0) {
+                tb.t_expert[t] = e;
+                tb.t_start[t] = s0;
+                tb.t_end[t] = s1;
+                ++t;
+            }
+        }
+        s_touched = t;
+    }
+    for (int p = threadIdx.x; p < A_rows; p += blockDim.x)
+        tb.src[p] = GATEUP ? perm[p] / K : p;
+    __syncthreads();
+
+    Shape S;
+    S.Kdim = Kdim;
+    S.N = N;
+    S.nsplit = nsplit;
+    S.ksplit = ksplit;
+    S.tiles = GATEUP ? 2 : 1;
+    S.groups = (N + 15) / 16;
+    S.steps = (ksplit + KSTEP - 1) / KSTEP;
+    S.total_items = uni(s_touched) * S.groups * nsplit;
+    S.NW = gridDim.x * WAVES;
+    if (gw >= S.total_items) return;
+
+    const uint32_t row_bytes = (uint32_t)Kdim * 2u;
+    const __amdgpu_buffer_rsrc_t a_rs = rsrc(A, (uint32_t)(A_src_rows * Kdim * 2));
+    const uint32_t w_bytes = (uint32_t)N * row_bytes;  // one expert's matrix
+    const uint32_t out_bytes = (uint32_t)((GATEUP ? 2 : 4) * (int64_t)nsplit * A_rows * N);
+    const __amdgpu_buffer_rsrc_t o_rs = rsrc(Cout, out_bytes);
+
+    // ---- weight rows: instruction i loads 1 KB of tile row i ------------------
+    Cursor bc = start_cursor(tb, S, gw);  // position of the rows being loaded
+    u32x4_t wq[16];
+    auto load_rows = [&]() {
+        const Where& w = bc.w;
+        const int k = w.kbeg + bc.step * KSTEP + lane * 8;
+        const bool ok = !KTAIL || k < w.kend;
+        const int kc = ok ? k : w.kend - 8;  // clamped, in range
+        const uint16_t* base = (GATEUP && bc.tile == 1) ? B3 : B1;
+        const __amdgpu_buffer_rsrc_t w_rs = rsrc(base + (int64_t)w.expert * N * Kdim, w_bytes);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        int col;
-        const uint16_t* base;
+        for (int i = 0; i < 16; ++i) {
+            const int col = min(w.col0 + i, N - 1);  // columns past N are never stored
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                w_rs, (uint32_t)col * row_bytes + (uint32_t)kc * 2u, 0, NT_AUX);
+            wq[i] = ok ? v : u32x4_t{0, 0, 0, 0};
+        }
+        step_on(tb, S, bc);
+    };
+    auto rows_to_lds = [&]() {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tile[lds_pos(i, lane)] = wq[i];
+    };
+
+    // ---- token fragments: fragment c, lane (token j16, group g) -> chunk 4c+g --
+    Cursor ac = start_cursor(tb, S, gw);  // position of the token fragments loaded
+    u32x4_t tq[16];
+    auto load_tokens = [&]() {
+        const Where& w = ac.w;
+        const int k0 = w.kbeg + ac.step * KSTEP;
+        const int p = min(ac.row0 + j16, w.end - 1);
+        // padding token lanes (past the expert's rows) read nothing: out of range -> 0
+        const uint32_t a_row = ac.row0 + j16 < w.end ? (uint32_t)tb.src[p] * row_bytes : OOB;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int k = k0 + (4 * c + g) * 8;
+            const bool ok = !KTAIL || k < w.kend;
+            const int kc = ok ? k : w.kend - 8;
+            const u32x4_t v =
+                __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_row + (uint32_t)kc * 2u, 0, 0);
+            tq[c] = ok ? v : u32x4_t{0, 0, 0, 0};
+        }
+        step_on(tb, S, ac);
+    };
+
+    // ---- compute -----------------------------------------------------------------
+    // Weights are the MFMA A operand, tokens the B operand: the 16x16
+    // accumulator of lane l, register r is output column 4*(l/16) + r of the
+    // slice for token row l%16, so a lane owns 4 contiguous output columns.
+    // gate/up: the W1 tile streams first; its sums move to `prev` while the
+    // W3 tile accumulates.  Four independent accumulation chains.
+    Cursor cc = start_cursor(tb, S, gw);
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc4[4] = {z, z, z, z}, prev = z;
+    auto mfma = [&]() {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const u32x4_t wf = tile[lds_pos(j16, 4 * c + g)];
+            acc4[c & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf), as_bf16x8(tq[c]),
+                                                                  acc4[c & 3], 0, 0, 0);
+        }
+    };
+    auto finish = [&]() {
+        const Where& w = cc.w;
+        const f32x4_t acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+        const bool tile_end = cc.valid && cc.step == S.steps - 1;
+        const bool last = tile_end && cc.tile == S.tiles - 1;
+        const int row = cc.row0 + j16;
+        const int col = w.col0 + 4 * g;
+        const bool ok = last && row < w.end && col < N;
         if (GATEUP) {
-            col = col0 + (t < NT / 2 ? t : t - NT / 2) * 16 + j;
-            base = t < NT / 2 ? B1 : B3;
+            u32x2_t h;
+            h.x = pack_bf16x2(silu(prev[0]) * acc[0], silu(prev[1]) * acc[1]);
+            h.y = pack_bf16x2(silu(prev[2]) * acc[2], silu(prev[3]) * acc[3]);
+            const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + col) * 2) : OOB;
+            __builtin_amdgcn_raw_buffer_store_b64(h, o_rs, off, 0, 0);
         } else {
-            col = col0 + t * 16 + j;
-            base = B1;
+            const int64_t o = ((int64_t)w.split * A_rows + row) * N + col;
+            const uint32_t off = ok ? (uint32_t)(o * 4) : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc), o_rs, off, 0,
+                                                   0);
         }
-        b_ok[t] = col < N;
-        b_ptr[t] = base + ((int64_t)e * N + (b_ok[t] ? col : 0)) * Kdim + g * 32;
+        prev = tile_end ? acc : prev;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc4[i] = tile_end ? z : acc4[i];
+        step_on(tb, S, cc);
+    };
+
+    // Steps in this wave's sequence (extra steps past the end repeat the last
+    // loads and store nothing: the cursors are no longer valid).
+    int nsteps = 0;
+    for (int it = gw; it < S.total_items; it += S.NW) {
+        const int ti = it / (S.groups * S.nsplit);
+        const int rows = uni(tb.t_end[ti]) - uni(tb.t_start[ti]);
+        nsteps += (rows + 15) / 16 * S.tiles * S.steps;
     }
-
-    for (int m0 = 0; m0 < M; m0 += 16) {
-        const int i = lane & 15;
-        const bool a_ok = m0 + i < M;
-        const int p = start + m0 + (a_ok ? i : 0);
-        const int64_t src = GATEUP ? (int64_t)(perm[p] / K) : (int64_t)p;
-        const uint16_t* a_ptr = A + src * Kdim + g * 32;
-
-        f32x4_t acc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        uint4 av0[4], bv0[NT][4], av1[4], bv1[NT][4];
-        auto load = [&](uint4(&av)[4], uint4(&bv)[NT][4], int k0) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool k_ok = k0 + g * 32 + c * 8 < kend;
-                av[c] = (a_ok && k_ok) ? *reinterpret_cast<const uint4*>(a_ptr + k0 + c * 8)
-                                       : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    bv[t][c] = (b_ok[t] && k_ok)
-                                   ? *reinterpret_cast<const uint4*>(b_ptr[t] + k0 + c * 8)
-                                   : make_uint4(0, 0, 0, 0);
-            }
-        };
-        auto compute = [&](const uint4(&av)[4], const uint4(&bv)[NT][4]) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(av[c]), as_bf16x8(bv[t][c]), acc[t], 0, 0, 0);
-        };
-
-        // two named register buffers, alternating, so every index is static
-        int k0 = kbeg;
-        load(av0, bv0, k0);
-        while (true) {
-            const bool more0 = k0 + KSTEP < kend;
-            if (more0) load(av1, bv1, k0 + KSTEP);
-            compute(av0, bv0);
-            if (!more0) break;
-            k0 += KSTEP;
-            const bool more1 = k0 + KSTEP < kend;
-            if (more1) load(av0, bv0, k0 + KSTEP);
-            compute(av1, bv1);
-            if (!more1) break;
-            k0 += KSTEP;
-        }
-
-        // 16x16 accumulator layout: lane l, register r holds row 4*(l/16) + r
-        // and column l%16 of the tile.
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * g + r;
-            if (m0 + row >= M) continue;
-            const int64_t orow = (int64_t)(start + m0 + row) * N;
-            if (GATEUP) {
-                uint16_t* H = static_cast<uint16_t*>(Cout);
-#pragma unroll
-                for (int t = 0; t < NT / 2; ++t) {
-                    const int col = col0 + t * 16 + j;
-                    if (col < N)
-                        H[orow + col] = f32_to_bf16_bits(silu(acc[t][r]) * acc[t + NT / 2][r]);
-                }
-            } else {
-                float* O = static_cast<float*>(Cout) + (int64_t)blockIdx.z * A_rows * N;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int col = col0 + t * 16 + j;
-                    if (col < N) O[orow + col] = acc[t][r];
-                }
-            }
-        }
+    load_rows();      // step 0 rows
+    load_tokens();    // step 0 tokens
+    rows_to_lds();    // (waits for step 0 rows)
+    load_rows();      // step 1 rows in flight
+    for (int q = 0; q < nsteps; ++q) {  // one back edge, no early exit
+        mfma();         // step q (LDS + token fragments)
+        rows_to_lds();  // step q+1 rows, loaded during step q
+        load_tokens();  // step q+1 tokens (issued before the rows of q+2)
+        load_rows();    // step q+2 rows stay in flight through step q+1
+        finish();       // epilogue store of step q (fixed instruction stream)
     }
-}
-
-int split_len(int Kdim, int splits) {
-    return ((Kdim + splits - 1) / splits + KSTEP - 1) / KSTEP * KSTEP;
-}
-
-template <bool GATEUP, int NT>
-hipError_t launch_skinny_t(const uint16_t* A, const int32_t* perm, int K, const uint16_t* B1,
-                           const uint16_t* B3, const int32_t* offsets, int n, int64_t A_rows,
-                           int Kdim, int N, void* C, int splits, hipStream_t s) {
-    constexpr int CW = GATEUP ? NT / 2 * 16 : NT * 16;
-    const int waves = 4;
-    const int ksplit = split_len(Kdim, splits);
-    const int zs = (Kdim + ksplit - 1) / ksplit;
-    const dim3 grid((unsigned)((N + waves * CW - 1) / (waves * CW)), (unsigned)n, (unsigned)zs);
-    hipLaunchKernelGGL((gemm_skinny_kernel<GATEUP, NT>), grid, dim3(waves * kWave), 0, s, A,
-                       perm, K, B1, B3, offsets, Kdim, N, C, ksplit, A_rows);
-    return hipGetLastError();
 }
 
 }  // namespace
 
-int skinny_splits_used(int Kdim, int splits) {
-    const int ksplit = split_len(Kdim, splits);
-    return (Kdim + ksplit - 1) / ksplit;
+int skinny_waves_per_cu() { return WAVES; }
+
+bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits) {
+    // every buffer range must stay below 2^31 bytes (32-bit buffer offsets)
+    const int64_t lim = int64_t(1) << 31;
+    return A_rows <= MAX_ROWS && A_src_rows * Kdim * 2 < lim && N * Kdim * 2 < lim &&
+           (int64_t)splits * A_rows * N * 4 < lim;
 }
 
-hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, const int32_t* perm, int K,
-                                   const uint16_t* B1, const uint16_t* B3,
-                                   const int32_t* offsets, int n, int64_t A_rows, int Kdim,
-                                   int N, void* C, int splits, hipStream_t s) {
-    if (gateup)
-        return launch_skinny_t<true, 2>(A, perm, K, B1, B3, offsets, n, A_rows, Kdim, N, C, 1,
-                                        s);
-    return launch_skinny_t<false, 2>(A, perm, K, B1, B3, offsets, n, A_rows, Kdim, N, C,
-                                     splits, s);
+hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src_rows,
+                                   const int32_t* perm, int K, const uint16_t* B1,
+                                   const uint16_t* B3, const int32_t* offsets, int n,
+                                   int64_t A_rows, int Kdim, int N, void* C, int splits, int cus,
+                                   hipStream_t s) {
+    const int ksplit = (((Kdim + splits - 1) / splits) + 7) / 8 * 8;
+    const int nsplit = (Kdim + ksplit - 1) / ksplit;
+    if (!skinny_fits(A_src_rows, A_rows, Kdim, N, splits)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cus), block((unsigned)(WAVES * kWave));
+    // every K split a whole number of steps: no partial chunks to zero
+    const bool ktail = (ksplit % KSTEP) != 0 || (Kdim % ksplit) != 0;
+#define MOE_SKINNY(GU, KT)                                                                 \
+    hipLaunchKernelGGL((gemm_skinny_kernel<GU, KT>), grid, block, 0, s, A, perm, K, B1, B3, \
+                       offsets, n, Kdim, N, C, A_rows, A_src_rows, nsplit, ksplit)
+    if (gateup) {
+        if (ktail) MOE_SKINNY(true, true);
+        else MOE_SKINNY(true, false);
+    } else {
+        if (ktail) MOE_SKINNY(false, true);
+        else MOE_SKINNY(false, false);
+    }
+#undef MOE_SKINNY
+    return hipGetLastError();
+}
+
+int skinny_splits_used(int Kdim, int splits) {
+    const int ksplit = (((Kdim + splits - 1) / splits) + 7) / 8 * 8;
+    return (Kdim + ksplit - 1) / ksplit;
 }
 
 }  // namespace moe
