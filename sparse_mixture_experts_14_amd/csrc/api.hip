@@ -68,21 +68,28 @@ int device_cus() {
     return cache[dev];
 }
 
-// K splits of the skinny down projection: the split count in [1, max_splits]
-// whose item count (all n experts touched) spreads most evenly over the
-// persistent waves; ties go to fewer splits.
-int choose_down_splits(int32_t n, int64_t d, int64_t d_ff, int max_splits, int waves) {
-    const int64_t groups = (d + 15) / 16;  // 16 output columns per item
-    int best = 1;
+// Waves per CU and K splits of a skinny GEMM: the pair whose item count
+// (all n experts touched; `groups` 16-column items per split) spreads most
+// evenly over the persistent waves; ties go to fewer splits, since longer
+// runs along each weight row stream faster.
+struct SkinnyShape {
+    int waves, splits;
+};
+SkinnyShape choose_skinny(int32_t n, int64_t N, int64_t Kdim, int max_splits, int cus) {
+    const int64_t groups = (N + 15) / 16;
+    SkinnyShape best{7, 1};
     double best_eff = -1.0;
     for (int s = 1; s <= max_splits; ++s) {
-        if (moe::skinny_splits_used((int)d_ff, s) != s) continue;
-        const int64_t items = (int64_t)n * groups * s;
-        const int64_t rounds = (items + waves - 1) / waves;
-        const double eff = (double)items / (double)(rounds * waves);
-        if (eff > best_eff + 1e-9) {
-            best_eff = eff;
-            best = s;
+        if (moe::skinny_splits_used((int)Kdim, s) != s) continue;
+        for (int w = 7; w <= 8; ++w) {
+            const int64_t items = (int64_t)n * groups * s;
+            const int64_t nw = (int64_t)cus * w;
+            const int64_t rounds = (items + nw - 1) / nw;
+            const double eff = (double)items / (double)(rounds * nw);
+            if (eff > best_eff + 1e-9) {
+                best_eff = eff;
+                best = {w, s};
+            }
         }
     }
     return best;
@@ -238,9 +245,12 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     const void* act = block ? u : x;
     int splits = 1;
     const int cus = device_cus();
-    if (bf16 && plan.skinny)
-        splits = choose_down_splits(n, d, d_ff, plan.down_splits,
-                                    cus * moe::skinny_waves_per_cu());
+    SkinnyShape sk_gu{7, 1}, sk_dn{7, 1};
+    if (bf16 && plan.skinny) {
+        sk_gu = choose_skinny(n, d_ff, d, 1, cus);
+        sk_dn = choose_skinny(n, d, d_ff, plan.down_splits, cus);
+        splits = sk_dn.splits;
+    }
     for (int stage = MOE_STAGE_GATE_UP; stage <= MOE_STAGE_DOWN; ++stage) {
         const bool gu = stage == MOE_STAGE_GATE_UP;
         const void* a_in = gu ? act : H;
@@ -262,7 +272,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                                    static_cast<const uint16_t*>(b1),
                                                    static_cast<const uint16_t*>(b3), offsets, n,
                                                    (int64_t)A, kdim, ndim, c_out,
-                                                   gu ? 1 : splits, cus, s);
+                                                   gu ? 1 : splits,
+                                                   gu ? sk_gu.waves : sk_dn.waves, cus, s);
             else
                 err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in), pm, K,
                                                   static_cast<const uint16_t*>(b1),

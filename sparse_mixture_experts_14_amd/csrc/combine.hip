@@ -5,7 +5,8 @@
 // GeekNews summary, "Implementasi dan Efisiensi Inferensi": expert outputs go
 // back to their tokens' original positions.
 //
-// Each token gathers its K expert rows (fp32, possibly split into S partial
+// One thread per 4 output columns (a workgroup covers 1024 columns of one
+// token).  Each token gathers its K expert rows (fp32, possibly split into S partial
 // sums of the down projection) and sums them in a fixed order -- partials in
 // split order, then slots in k order -- so the result is deterministic and no
 // atomics are needed.  The sum is rounded once into the output dtype (RNE).
@@ -21,9 +22,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ O, int64_t A, int S, const int32_t* __restrict__ inv,
     const float* __restrict__ gate, int K, int d, const TOut* __restrict__ resid,
     TOut* __restrict__ y) {
-    const int64_t t = blockIdx.x;
+    const int cb = (d + 1023) / 1024;  // workgroups per token
+    const int64_t t = blockIdx.x / cb;
     const int64_t split_stride = A * (int64_t)d;
-    for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    const int c = (int)(blockIdx.x % cb) * 1024 + threadIdx.x * 4;
+    if (c < d) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k = 0; k < K; ++k) {
             const int64_t pos = inv[t * K + k];
@@ -76,8 +79,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int S,
                           const int32_t* inv, const float* gate, int64_t T, int K, int d,
                           const void* x, void* y, hipStream_t s) {
-    const dim3 grid((unsigned)T);
-    const dim3 block(d >= 1024 ? 256 : 64);
+    const int64_t cb = (d + 1023) / 1024;
+    if (T * cb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(T * cb));
+    const dim3 block(256);
     if (bf16) {
         if (resid)
             hipLaunchKernelGGL((combine_kernel<uint16_t, true>), grid, block, 0, s, O, A, S,

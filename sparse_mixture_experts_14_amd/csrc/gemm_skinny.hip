@@ -11,9 +11,10 @@
 //   one of S K-splits (partial sums go to O + s * A_rows * N and the combine
 //   stage adds the S splits in order).  Items of experts with no rows do not
 //   exist (an expert whose gate is 0 is never read).  The grid is
-//   persistent: one workgroup of W waves per CU (its LDS keeps a second one
-//   off the CU) and wave g takes items g, g + NW, ...; the host picks S so
-//   that items divide evenly over the waves.
+//   persistent: one workgroup of W (7 or 8) waves per CU (its LDS keeps a
+//   second one off the CU) and wave g takes items g, g + NW, ...; the host
+//   picks W and S so that items divide evenly over the waves, preferring
+//   fewer splits (longer runs along each weight row).
 // * Weight loads.  HBM streams best in long runs per row, so every load
 //   instruction reads 1 KB of one weight row (lane l: elements 8l..8l+7 of a
 //   512-element step), non-temporal, into registers; the wave then writes the
@@ -47,7 +48,6 @@ namespace {
 
 
 constexpr int KSTEP = 512;         // k per step: 64 lanes x 8 elements of one row
-constexpr int WAVES = 7;           // waves per workgroup (= per CU)
 constexpr int MAX_ROWS = 2048;     // row-source table in LDS (the host keeps A <= this)
 constexpr int TILE_U4 = 16 * 64;   // one wave's LDS tile: 16 rows x 64 chunks of 16 bytes
 
@@ -132,7 +132,7 @@ constexpr int NT_AUX = 2;              // non-temporal cache policy
 // LDS position (in 16-byte units) of chunk q of tile row r.
 __device__ __forceinline__ int lds_pos(int r, int q) { return r * 64 + (q ^ r); }
 
-template <bool GATEUP, bool KTAIL>
+template <bool GATEUP, bool KTAIL, int WAVES>
 __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm, int K,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
@@ -294,8 +294,6 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
 
 }  // namespace
 
-int skinny_waves_per_cu() { return WAVES; }
-
 bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits) {
     // every buffer range must stay below 2^31 bytes (32-bit buffer offsets)
     const int64_t lim = int64_t(1) << 31;
@@ -306,24 +304,28 @@ bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, in
 hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                    const int32_t* perm, int K, const uint16_t* B1,
                                    const uint16_t* B3, const int32_t* offsets, int n,
-                                   int64_t A_rows, int Kdim, int N, void* C, int splits, int cus,
-                                   hipStream_t s) {
+                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
+                                   int waves, int cus, hipStream_t s) {
     const int ksplit = (((Kdim + splits - 1) / splits) + 7) / 8 * 8;
     const int nsplit = (Kdim + ksplit - 1) / ksplit;
-    if (!skinny_fits(A_src_rows, A_rows, Kdim, N, splits)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)cus), block((unsigned)(WAVES * kWave));
+    if (!skinny_fits(A_src_rows, A_rows, Kdim, N, nsplit)) return hipErrorInvalidValue;
+    if (waves != 7 && waves != 8) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cus), block((unsigned)(waves * kWave));
     // every K split a whole number of steps: no partial chunks to zero
     const bool ktail = (ksplit % KSTEP) != 0 || (Kdim % ksplit) != 0;
-#define MOE_SKINNY(GU, KT)                                                                 \
-    hipLaunchKernelGGL((gemm_skinny_kernel<GU, KT>), grid, block, 0, s, A, perm, K, B1, B3, \
-                       offsets, n, Kdim, N, C, A_rows, A_src_rows, nsplit, ksplit)
+#define MOE_SKINNY(GU, KT, W)                                                               \
+    hipLaunchKernelGGL((gemm_skinny_kernel<GU, KT, W>), grid, block, 0, s, A, perm, K, B1, \
+                       B3, offsets, n, Kdim, N, C, A_rows, A_src_rows, nsplit, ksplit)
+#define MOE_SKINNY_W(GU, KT) \
+    if (waves == 7) MOE_SKINNY(GU, KT, 7); else MOE_SKINNY(GU, KT, 8)
     if (gateup) {
-        if (ktail) MOE_SKINNY(true, true);
-        else MOE_SKINNY(true, false);
+        if (ktail) { MOE_SKINNY_W(true, true); }
+        else { MOE_SKINNY_W(true, false); }
     } else {
-        if (ktail) MOE_SKINNY(false, true);
-        else MOE_SKINNY(false, false);
+        if (ktail) { MOE_SKINNY_W(false, true); }
+        else { MOE_SKINNY_W(false, false); }
     }
+#undef MOE_SKINNY_W
 #undef MOE_SKINNY
     return hipGetLastError();
 }

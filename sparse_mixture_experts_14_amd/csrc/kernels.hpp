@@ -27,19 +27,18 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, const int32_t*
                                   int N, void* C, hipStream_t s);
 
 // bf16 MFMA grouped GEMMs streaming weights (few rows per expert), one
-// persistent workgroup of skinny_waves_per_cu() waves per CU (`cus` of them).
+// persistent workgroup of `waves` (7 or 8) waves per CU (`cus` of them).
 // The down projection may split K into partial sums; skinny_splits_used()
 // tells how many splits a request of `splits` really produces.
 hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                    const int32_t* perm, int K, const uint16_t* B1,
                                    const uint16_t* B3, const int32_t* offsets, int n,
-                                   int64_t A_rows, int Kdim, int N, void* C, int splits, int cus,
-                                   hipStream_t s);
+                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
+                                   int waves, int cus, hipStream_t s);
 // Whether the skinny kernels can take these sizes (row table in LDS, 32-bit
 // buffer offsets).
 bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits);
 int skinny_splits_used(int Kdim, int splits);
-int skinny_waves_per_cu();
 
 // y = sum_k gate * (sum over S splits of O) (+ x), rounded once.
 hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int S,

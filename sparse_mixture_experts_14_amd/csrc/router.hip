@@ -4,11 +4,12 @@
 // G(x) = Softmax(TopK(x . W_g)); TopK leaves the K largest logits and sets the
 // rest to -inf, so the softmax normalises over the K kept logits only.
 //
-// One wavefront per token.  Lane l reads the 16-byte chunks l, l+64, ... of the
-// token's row, multiplies each element with the matching row of W_g (n
-// contiguous values), and keeps n fp32 partial sums.  A butterfly reduction
-// gives every lane the same n logits (fp32, never rounded to bf16); the TopK
-// (ties to the lower index) and the softmax are then evaluated per wave.
+// One workgroup of 256 threads per token.  Thread i reads the 16-byte chunks
+// i, i+256, ... of the token's row, multiplies each element with the matching
+// row of W_g (n contiguous values), and keeps n fp32 partial sums; a butterfly
+// inside each wave and a fixed-order sum of the 4 waves' partials in LDS give
+// the n logits (fp32, never rounded to bf16, same order every call).  Thread
+// 0 then takes the TopK (ties to the lower index) and the softmax.
 //
 // The pre-normalised variant (a layer of a residual stack) also accumulates
 // sum(x^2), scales the logits by rstd = 1/sqrt(mean(x^2) + eps) -- the same
@@ -83,9 +84,12 @@ __global__ __launch_bounds__(256) void router_kernel(
     int K, float eps, int32_t* __restrict__ idx, float* __restrict__ gate,
     TIn* __restrict__ u_out) {
     constexpr int VN = Vec<TIn>::N;
+    constexpr int NTH = 256;
+    __shared__ float part[NTH / kWave][NE + 1];
+    __shared__ float s_rstd;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    if (t >= T) return;
+    const int wv = threadIdx.x / kWave;
+    const int64_t t = blockIdx.x;
     const TIn* __restrict__ xr = x + t * (int64_t)d;
 
     float acc[NE];
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void router_kernel(
     float ss = 0.0f;
 
     // d is a multiple of 8, so every chunk is either whole or absent.
-    for (int k0 = lane * VN; k0 < d; k0 += kWave * VN) {
+    for (int k0 = threadIdx.x * VN; k0 < d; k0 += NTH * VN) {
         float xv[VN];
         Vec<TIn>::load(xr + k0, xv);
 #pragma unroll
@@ -105,15 +109,27 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = wave_sum(acc[e]);
-    float rstd = 1.0f;
-    if (NORM) {
-        ss = wave_sum(ss);
-        rstd = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[e] *= rstd;
-    }
-
+    if (NORM) ss = wave_sum(ss);
     if (lane == 0) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) part[wv][e] = acc[e];
+        part[wv][NE] = ss;
+    }
+    __syncthreads();
+
+    if (threadIdx.x == 0) {
+        float l[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            l[e] = (part[0][e] + part[1][e]) + (part[2][e] + part[3][e]);
+        float rstd = 1.0f;
+        if (NORM) {
+            const float sst = (part[0][NE] + part[1][NE]) + (part[2][NE] + part[3][NE]);
+            rstd = 1.0f / sqrtf(sst / (float)d + eps);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) l[e] *= rstd;
+            s_rstd = rstd;
+        }
         // TopK: K rounds of "largest logit not yet taken"; a later expert
         // needs a strictly larger logit, so ties go to the lower index.
         uint64_t taken = 0;
@@ -127,9 +143,9 @@ __global__ __launch_bounds__(256) void router_kernel(
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
                     if (e < n && !((taken >> e) & 1ull)) {
-                        if (best < 0 || acc[e] > bv) {
+                        if (best < 0 || l[e] > bv) {
                             best = e;
-                            bv = acc[e];
+                            bv = l[e];
                         }
                     }
                 }
@@ -159,8 +175,10 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
 
     if (NORM) {
+        __syncthreads();
+        const float rstd = s_rstd;
         TIn* __restrict__ ur = u_out + t * (int64_t)d;
-        for (int k0 = lane * VN; k0 < d; k0 += kWave * VN) {
+        for (int k0 = threadIdx.x * VN; k0 < d; k0 += NTH * VN) {
             float xv[VN];
             Vec<TIn>::load(xr + k0, xv);
 #pragma unroll
@@ -174,9 +192,8 @@ template <typename TIn, bool NORM>
 hipError_t launch_router_t(const void* x, const void* wg, int64_t T, int d, int n, int K,
                            float eps, int32_t* idx, float* gate, void* u_out,
                            hipStream_t s) {
-    const int wpb = 4;
-    const dim3 grid((unsigned)((T + wpb - 1) / wpb));
-    const dim3 block(wpb * kWave);
+    const dim3 grid((unsigned)T);
+    const dim3 block(256);
     const TIn* xp = static_cast<const TIn*>(x);
     const TIn* wp = static_cast<const TIn*>(wg);
     TIn* up = static_cast<TIn*>(u_out);
