@@ -193,6 +193,11 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: optional outputs must be 4-byte aligned", fn);
     if (dt == MOE_F32 && (int64_t)T * K / 64 + n > 65535)
         return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 path supports T * K < 4M", fn);
+    if (dt == MOE_BF16 && (!moe::tiled_fits(T, d, d_ff) || !moe::tiled_fits((int64_t)T * K, d_ff, d)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: bf16 operands must stay below 2 GiB (T*d, T*K*d_ff, d*d_ff elements "
+                    "< 2^30); split the tokens into several calls",
+                    fn);
     const Layout L = layout(T, d, d_ff, n, K, dt);
     if (T > 0) {
         if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
@@ -275,7 +280,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                                    gu ? 1 : splits,
                                                    gu ? sk_gu.waves : sk_dn.waves, cus, s);
             else
-                err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in), pm, K,
+                err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in),
+                                                  gu ? T : (int64_t)A, pm, K,
                                                   static_cast<const uint16_t*>(b1),
                                                   static_cast<const uint16_t*>(b3), offsets, n,
                                                   (int64_t)A, kdim, ndim, c_out, s);

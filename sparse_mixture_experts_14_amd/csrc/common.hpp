@@ -51,6 +51,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
 // SiLU(z) = z / (1 + e^-z) (Swish with beta = 1).
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Same function with the hardware exp2 and reciprocal (a few ulp of fp32),
+// for results that are rounded to bf16 (8 mantissa bits) right after.
+__device__ __forceinline__ float silu_bf16out(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // Sum over the 64 lanes of a wavefront.  Butterfly order: every lane ends with
 // the bitwise-identical total.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -255,8 +255,8 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
         const bool ok = last && row < w.end && col < N;
         if (GATEUP) {
             u32x2_t h;
-            h.x = pack_bf16x2(silu(prev[0]) * acc[0], silu(prev[1]) * acc[1]);
-            h.y = pack_bf16x2(silu(prev[2]) * acc[2], silu(prev[3]) * acc[3]);
+            h.x = pack_bf16x2(silu_bf16out(prev[0]) * acc[0], silu_bf16out(prev[1]) * acc[1]);
+            h.y = pack_bf16x2(silu_bf16out(prev[2]) * acc[2], silu_bf16out(prev[3]) * acc[3]);
             const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + col) * 2) : OOB;
             __builtin_amdgcn_raw_buffer_store_b64(h, o_rs, off, 0, 0);
         } else {

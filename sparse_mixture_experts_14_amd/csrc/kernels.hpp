@@ -20,11 +20,14 @@ hipError_t launch_gemm_f32(bool gateup, const float* A, const int32_t* perm, int
                            const float* B1, const float* B3, const int32_t* offsets, int n,
                            int64_t A_rows, int Kdim, int N, float* C, hipStream_t s);
 
-// bf16 MFMA grouped GEMMs, LDS-tiled (many rows per expert).
-hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, const int32_t* perm, int K,
-                                  const uint16_t* B1, const uint16_t* B3,
-                                  const int32_t* offsets, int n, int64_t A_rows, int Kdim,
-                                  int N, void* C, hipStream_t s);
+// bf16 MFMA grouped GEMMs, LDS-tiled (many rows per expert).  A has
+// A_src_rows rows of Kdim elements (x, u or H).
+hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,
+                                  const int32_t* perm, int K, const uint16_t* B1,
+                                  const uint16_t* B3, const int32_t* offsets, int n,
+                                  int64_t A_rows, int Kdim, int N, void* C, hipStream_t s);
+// Whether the tiled kernels can take these sizes (32-bit buffer offsets).
+bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N);
 
 // bf16 MFMA grouped GEMMs streaming weights (few rows per expert), one
 // persistent workgroup of `waves` (7 or 8) waves per CU (`cus` of them).
