@@ -49,9 +49,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 // projection uses.  Depends on sizes only (so the workspace bound holds); the
 // environment variable MOE_GEMM_PATH=tiled|skinny forces a bf16 path (a
 // testing and tuning knob).
-// Upper bound of the K splits of the skinny down projection (partial sums in
-// the workspace): splits only pay off with few rows.
-int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 1; }
+// Upper bound of the K splits of the down projection (partial sums in the
+// workspace): up to 8 for the skinny kernel (few rows), 2 for the tiled one.
+int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 2; }
 
 // Compute units of the current device (cached per device id).
 int device_cus() {
@@ -255,6 +255,9 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
         sk_gu = choose_skinny(n, d_ff, d, 1, cus);
         sk_dn = choose_skinny(n, d, d_ff, plan.down_splits, cus);
         splits = sk_dn.splits;
+    } else if (bf16) {
+        splits = moe::tiled_down_splits((int64_t)A, n, (int)d, (int)d_ff, cus,
+                                        requested_down_splits(T, K));
     }
     for (int stage = MOE_STAGE_GATE_UP; stage <= MOE_STAGE_DOWN; ++stage) {
         const bool gu = stage == MOE_STAGE_GATE_UP;
@@ -284,7 +287,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                                   gu ? T : (int64_t)A, pm, K,
                                                   static_cast<const uint16_t*>(b1),
                                                   static_cast<const uint16_t*>(b3), offsets, n,
-                                                  (int64_t)A, kdim, ndim, c_out, s);
+                                                  (int64_t)A, kdim, ndim, c_out,
+                                                  gu ? 1 : splits, s);
         }
         mark(g_ev_end[stage]);
         if (err != hipSuccess) return hip_fail(err, gu ? "gate/up GEMM launch" : "down GEMM launch");

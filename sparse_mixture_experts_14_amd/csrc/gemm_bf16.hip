@@ -1,35 +1,36 @@
 // Grouped expert GEMMs on bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16), fp32
-// accumulation, LDS-staged double-buffered tiles (many rows per expert).
+// accumulation, LDS-staged tiles filled by direct global->LDS loads (many rows
+// per expert).
 //
 // Expert FFN of "Mixtral of Experts" (xyznot digest, "Method" section and
 // "Key terms"): SwiGLU_e(u) = W2_e (SiLU(W1_e u) (*) W3_e u).  The GeekNews
 // summary ("Implementasi dan Efisiensi Inferensi") describes running all
 // experts as one grouped product over an uneven number of tokens per expert;
 // here the rows of every expert are contiguous after the permutation stage
-// and a workgroup owns one BM x BN tile of one expert.
+// and a workgroup owns one 256 x 256 tile of one expert.
 //
 //   gate/up:  H[p][f] = bf16( SiLU(u_p . W1_e[f]) * (u_p . W3_e[f]) )
 //             A rows are gathered, u_p = x[perm[p] / K]; the B tile holds
-//             BN/2 rows of W1 and the same BN/2 rows of W3, so the SiLU*mul
+//             128 rows of W1 and the same 128 rows of W3, so the SiLU*mul
 //             epilogue finds both accumulators in the same lane.
-//   down:     O[p][c] = H_p . W2_e[c]   (fp32 out)
+//   down:     O[s][p][c] = sum over the K range of split s of H_p . W2_e[c]
+//             (fp32 partial sums; the combine stage adds the splits).
 //
 // Tile shape.  256 x 256 accumulator tile, 4 waves, each 128 x 128 (4 x 4
-// MFMA tiles of 32 x 32, 256 fp32 accumulators per lane): per 16-element K
-// sub-step a wave reads 4 A and 4 B fragments from LDS for 16 MFMAs, and a
-// workgroup fetches 64 KB from L2 per 64-element K step for 2 * 256^3 / 4 =
-// 8.4 Mflop -- the arithmetic intensity that keeps the L2 ahead of the MFMAs.
-// Both operands are K-contiguous ([out][in] weights), which is the per-lane
-// 8-element K run each MFMA operand wants; LDS rows are 64 bf16 (8 chunks of
-// 16 bytes) with the chunk index XOR-swizzled by (row >> 1) & 7, so the
-// 16-byte LDS reads of 16 consecutive rows and the row-wise writes hit
-// distinct banks.
+// MFMA tiles of 32 x 32, 256 fp32 accumulators per lane, in AGPRs): per
+// 16-element K sub-step a wave reads 4 A and 4 B fragments from LDS for 16
+// MFMAs.  Both operands are K-contiguous ([out][in] weights), which is the
+// per-lane 8-element K run each MFMA operand wants.  The weights are the
+// MFMA's first operand, so a lane ends up owning 4 contiguous output columns.
 //
-// Pipeline.  Two LDS stages plus one register stage: the global loads of K
-// step k+1 are issued before the MFMAs of step k and land in LDS after them.
-// Loads go through buffer resources with 32-bit offsets and are
-// unconditional (rows past the tile are clamped to a valid row, never
-// stored); a K tail (rare shapes) zeroes the chunks past the end.
+// Pipeline.  NSTAGE LDS stages of BK-deep A and B tiles.  Each stage is filled
+// by buffer loads with the LDS flag (global -> LDS, no registers, no LDS
+// write instructions), issued NSTAGE - 1 steps ahead; one barrier per K step
+// waits only for the loads of the next step.  LDS rows are BK bf16 with the
+// 16-byte chunk XOR-swizzled so that the fragment reads of 16 consecutive
+// rows hit distinct banks.  Rows past the tile are clamped to a valid row
+// (never stored); a K tail and the padded steps past the end load through an
+// out-of-range offset, which writes zeros.
 //
 // Tile order: the 1-D grid is first spread over the 8 XCDs (block b runs on
 // XCD b % 8, so consecutive logical tiles go to one XCD and share its L2),
@@ -41,45 +42,63 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 64;  // K per LDS stage (8 chunks of 8 bf16)
-constexpr int CHUNKS = BK / 8;
-
-// Two 128-byte rows span the 64 banks; XOR-ing the chunk with (row >> 1) & 7
-// gives the 16 rows read by one 16-lane group 16 distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                              (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff),
                                              0x00020000);
 }
 
-template <bool GATEUP, bool KTAIL, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN* kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// s_waitcnt immediate: vector-memory count vm (6 bits, split), LDS count lgkm,
+// export count left at its maximum.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+template <int J>
+__device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
+                                         uint8_t* s4) {
+    if constexpr (J == 0) return s0;
+    if constexpr (J == 1) return s1;
+    if constexpr (J == 2) return s2;
+    if constexpr (J == 3) return s3;
+    return s4;
+}
+
+template <bool GATEUP, bool KTAIL, int BK, int NSTAGE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
-                      int n, int Kdim, int N, void* __restrict__ Cout, int mslots, int GM) {
-    constexpr int NTH = WM * WN * kWave;
+                      int n, int Kdim, int N, void* __restrict__ Cout, int mslots, int GM,
+                      int splits, int64_t split_stride) {
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 2, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (accumulator space)
     constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 MFMA tiles per wave
     constexpr int BNO = GATEUP ? BN / 2 : BN;     // output columns per tile
-    constexpr int A_LD = BM * CHUNKS / NTH;       // 16-byte chunks per thread
-    constexpr int B_LD = BN * CHUNKS / NTH;
-    constexpr int ROWS_PER_PASS = NTH / CHUNKS;   // rows a loader pass covers
-    static_assert(A_LD * NTH == BM * CHUNKS && B_LD * NTH == BN * CHUNKS, "tile/threads");
+    constexpr int KSUB = BK / 16;                 // MFMA sub-steps per K step
+    constexpr int ROW_BYTES = BK * 2;             // one LDS row: BK bf16
+    constexpr int CH = ROW_BYTES / 16;            // 16-byte chunks per row
+    constexpr int RPB = 256 / ROW_BYTES;          // rows per 256-byte bank sweep
+    constexpr int A_BYTES = BM * ROW_BYTES;       // A tile of one stage
+    constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+    static_assert(KSUB % 2 == 0 && NSTAGE >= 2 && NSTAGE <= 5, "pipeline shape");
     static_assert(!GATEUP || (TN % 2 == 0), "gate/up needs W1 and W3 tiles in pairs");
-    static_assert(!GATEUP || ((BN / 2) % ROWS_PER_PASS == 0), "W1/W3 split on a pass boundary");
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+    // One object per stage (A tile, then B tile), so that the compiler can
+    // tell the stage being read from the stages being filled.
+    __shared__ __attribute__((aligned(1024))) uint8_t S0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t S1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t S2[NSTAGE > 2 ? STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t S3[NSTAGE > 3 ? STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t S4[NSTAGE > 4 ? STAGE_BYTES : 16];
 
     // ---- tile coordinates -------------------------------------------------
-    const int G = gridDim.x;  // a multiple of 8
+    const int G = gridDim.x;  // splits x G1, G1 a multiple of 8
     const int b = blockIdx.x;
-    const int L = (b & 7) * (G >> 3) + (b >> 3);
+    const int L0 = (b & 7) * (G >> 3) + (b >> 3);
+    const int G1 = G / splits;
+    const int ks = L0 / G1;  // K split of this block
+    const int L = L0 - ks * G1;
     const int ntiles_n = (N + BNO - 1) / BNO;
     const int group = L / (GM * ntiles_n);
     const int first_m = group * GM;
@@ -95,73 +114,106 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wid % WM, wn = wid / WM;
 
-    // ---- loader setup: rows r0 + ROWS_PER_PASS * i, one 16-byte chunk -------
-    const int lr0 = tid / CHUNKS, lc = tid % CHUNKS;
-    const uint32_t row_bytes = (uint32_t)Kdim * 2u;
+    // ---- loader: global -> LDS without registers -----------------------------
+    // A buffer load with the LDS flag writes lane l's 16 bytes at LDS address
+    // M0 + 16 l, so one instruction fills 1 KB = ROWS_LD consecutive LDS rows.
+    // Lane l serves row ROWS_LD q + l / CH and physical chunk l % CH, i.e. the
+    // logical chunk (l % CH) ^ swizzle(row): it fetches exactly the 16 bytes
+    // that belong there, and the CH lanes of a row together read its K slice.
+    // Each wave issues A_LD + B_LD such loads per K step.
+    constexpr int ROWS_LD = 1024 / ROW_BYTES;          // rows per load instruction
+    constexpr int A_LD = BM / ROWS_LD / NW;            // A loads per wave per K step
+    constexpr int B_LD = BN / ROWS_LD / NW;
+    constexpr int NLD = A_LD + B_LD;
+    static_assert(A_LD * ROWS_LD * NW == BM && B_LD * ROWS_LD * NW == BN, "loader split");
+    static_assert(!GATEUP || B_LD % 2 == 0, "W1 and W3 halves of the B tile");
+    static_assert(NLD <= TM * TN, "loads fit between the first sub-step's MFMAs");
+    const int rr = lane / CH, pc = lane % CH;
+    const uint32_t src_row_bytes = (uint32_t)Kdim * 2u;
     const __amdgpu_buffer_rsrc_t a_rs = rsrc(A, A_src_rows * (int64_t)Kdim * 2);
     const int64_t wbytes = (int64_t)N * Kdim * 2;
     const __amdgpu_buffer_rsrc_t b1_rs = rsrc(B1 + (int64_t)e * N * Kdim, wbytes);
     const __amdgpu_buffer_rsrc_t b3_rs = GATEUP ? rsrc(B3 + (int64_t)e * N * Kdim, wbytes) : b1_rs;
+    const __amdgpu_buffer_rsrc_t null_rs = rsrc(A, 0);
+    // first LDS row of load i (A, B)
+    auto a_lrow = [&](int i) { return (wid * A_LD + i) * ROWS_LD; };
+    auto b_lrow = [&](int i) {
+        if (!GATEUP) return (wid * B_LD + i) * ROWS_LD;
+        constexpr int H = B_LD / 2;  // loads i < H: W1 rows, i >= H: the matching W3 rows
+        return (i < H ? 0 : BN / 2) + (wid * H + (i < H ? i : i - H)) * ROWS_LD;
+    };
     uint32_t a_off[A_LD], b_off[B_LD];
+    int a_k8[A_LD], b_k8[B_LD];  // first K element of the lane's chunk (tails only)
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int r = lr0 + ROWS_PER_PASS * i;
+        const int r = a_lrow(i) + rr;
+        const int c = pc ^ ((r / RPB) % CH);
         const int p = row0 + min(r, rows - 1);  // rows past the tile: a valid row, never stored
         const uint32_t src = GATEUP ? (uint32_t)(perm[p] / K) : (uint32_t)p;
-        a_off[i] = src * row_bytes + (uint32_t)lc * 16u;
+        a_off[i] = src * src_row_bytes + (uint32_t)c * 16u;
+        a_k8[i] = c * 8;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-        const int r = lr0 + ROWS_PER_PASS * i;
+        const int r = b_lrow(i) + rr;
+        const int c = pc ^ ((r / RPB) % CH);
         const int col = n0 + (GATEUP && r >= BN / 2 ? r - BN / 2 : r);
-        b_off[i] = (uint32_t)min(col, N - 1) * row_bytes + (uint32_t)lc * 16u;
+        b_off[i] = (uint32_t)min(col, N - 1) * src_row_bytes + (uint32_t)c * 16u;
+        b_k8[i] = c * 8;
     }
-
-    auto load_global = [&](int k0, u32x4_t(&ra)[A_LD], u32x4_t(&rb)[B_LD]) {
-        const bool ok = !KTAIL || (k0 + lc * 8 < Kdim);
-        const uint32_t kb = (uint32_t)(ok ? k0 : 0) * 2u;  // clamped in range
+    // K steps [k_begin, k_end) of this split
+    const int nk_all = (Kdim + BK - 1) / BK;
+    const int per_split = (nk_all + splits - 1) / splits;
+    const int k_begin = min(nk_all, ks * per_split);
+    const int k_end = min(nk_all, k_begin + per_split);
+    // Loads of K step kt into stage `st`.  Steps past the end go through a
+    // zero-size resource: every load is out of range and writes zeros, so the
+    // step count can be padded to a multiple of NSTAGE with exact results and
+    // an unchanged load count.  K tails: chunks past Kdim are out of range.
+    auto issue = [&](uint8_t* st, int kt) {
+        const bool live = kt < k_end;
+        const int k0 = live ? kt * BK : 0;
+        const uint32_t kb = (uint32_t)k0 * 2u;
+        const __amdgpu_buffer_rsrc_t ars = live ? a_rs : null_rs;
+        const __amdgpu_buffer_rsrc_t brs1 = live ? b1_rs : null_rs;
+        const __amdgpu_buffer_rsrc_t brs3 = live ? b3_rs : null_rs;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i] + kb, 0, 0);
-            ra[i] = ok ? v : u32x4_t{0, 0, 0, 0};
+            const uint32_t off = KTAIL && k0 + a_k8[i] >= Kdim ? 0x80000000u : a_off[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ars, (__attribute__((address_space(3))) void*)(st + a_lrow(i) * ROW_BYTES), 16,
+                off, kb, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
-            // compile-time: passes i >= (BN/2) / ROWS_PER_PASS hold the W3 rows
-            constexpr int W3_FROM = (BN / 2) / ROWS_PER_PASS;
-            const bool second = GATEUP && i >= W3_FROM;
-            const u32x4_t v =
-                __builtin_amdgcn_raw_buffer_load_b128(second ? b3_rs : b1_rs, b_off[i] + kb, 0, 0);
-            rb[i] = ok ? v : u32x4_t{0, 0, 0, 0};
+            const uint32_t off = KTAIL && k0 + b_k8[i] >= Kdim ? 0x80000000u : b_off[i];
+            const bool second = GATEUP && i >= B_LD / 2;  // compile-time
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                second ? brs3 : brs1,
+                (__attribute__((address_space(3))) void*)(st + A_BYTES + b_lrow(i) * ROW_BYTES),
+                16, off, kb, 0, 0);
         }
-    };
-    auto store_lds = [&](int st, const u32x4_t(&ra)[A_LD], const u32x4_t(&rb)[B_LD]) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            *reinterpret_cast<u32x4_t*>(&As[st][swz(lr0 + ROWS_PER_PASS * i, lc)]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            *reinterpret_cast<u32x4_t*>(&Bs[st][swz(lr0 + ROWS_PER_PASS * i, lc)]) = rb[i];
     };
 
     // ---- MFMA read coordinates ----------------------------------------------
+    // Every row a lane reads is congruent to l32 modulo 32, so its swizzle is
+    // the lane's own constant: fragment (i, sub-step kk) sits at a per-lane
+    // base plus kofs[kk] plus a compile-time row offset.
     const int l32 = lane & 31, khalf = lane >> 5;
-    int a_row[TM], b_row[TN];
+    const int sw = (l32 / RPB) % CH;
+    uint32_t kofs[KSUB];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a_row[i] = wm * WTM + i * 32 + l32;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        if (GATEUP) {
-            const int half = TN / 2;
-            const int jj = j < half ? j : j - half;
-            b_row[j] = (j < half ? 0 : BN / 2) + wn * (WTN / 2) + jj * 32 + l32;
-        } else {
-            b_row[j] = wn * WTN + j * 32 + l32;
-        }
-    }
+    for (int kk = 0; kk < KSUB; ++kk) kofs[kk] = (uint32_t)(((kk * 2 + khalf) ^ sw) << 4);
+    const uint32_t a_rd = (uint32_t)(wm * WTM + l32) * ROW_BYTES;
+    const uint32_t b_rd = A_BYTES + (uint32_t)(wn * (GATEUP ? WTN / 2 : WTN) + l32) * ROW_BYTES;
+    auto b_frag_row = [](int j) {  // first B row of fragment j, relative to the wave's rows
+        if (!GATEUP) return j * 32;
+        constexpr int half = TN / 2;
+        return (j < half ? 0 : BN / 2) + (j < half ? j : j - half) * 32;
+    };
 
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -171,15 +223,15 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (Kdim + BK - 1) / BK;
-    auto read_frags = [&](int st, int kk, bf16x8_t(&av)[TM], bf16x8_t(&bv)[TN]) {
-        const int ch = kk * 2 + khalf;
+    auto read_frags = [&](const uint8_t* st, int kk, bf16x8_t(&av)[TM], bf16x8_t(&bv)[TN]) {
+        const uint8_t* pa = st + a_rd + kofs[kk];
+        const uint8_t* pb = st + b_rd + kofs[kk];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            av[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&As[st][swz(a_row[i], ch)]));
+            av[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pa + i * 32 * ROW_BYTES));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            bv[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&Bs[st][swz(b_row[j], ch)]));
+            bv[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pb + b_frag_row(j) * ROW_BYTES));
     };
     auto mfmas = [&](const bf16x8_t(&av)[TM], const bf16x8_t(&bv)[TN]) {
 #pragma unroll
@@ -189,56 +241,70 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0,
                                                                     0, 0);
     };
-    // Scheduling hints (group masks: 0x008 MFMA, 0x020 global read, 0x100
-    // LDS read, 0x200 LDS write): spread each sub-step's fragment reads for
-    // the next sub-step between its MFMAs so LDS latency hides behind them.
-    // The reads go out during the first MFMAs, leaving the rest of the
-    // sub-step to cover their latency.
-    auto interleave_reads = [&]() {
+    // Scheduling hints (group masks: 0x008 MFMA, 0x020 VMEM read, 0x100 LDS
+    // read): the LDS reads of the next sub-step go out one per MFMA at the
+    // start of a sub-step, so their latency hides behind the remaining MFMAs;
+    // the first sub-step of a step also carries the loads of a later step.
+    auto interleave = [&](int nloads) {
 #pragma unroll
-        for (int q = 0; q < TM + TN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int q = 0; q < TM * TN; ++q) {
+            if (q < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (q < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+    };
+    // Block-wide barrier that only waits for this wave's loads of the step
+    // about to be read (the NSTAGE - 2 later steps' loads stay in flight) and
+    // for its own LDS reads (the stage they read is refilled after it).
+    auto barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NSTAGE - 2) * NLD, 0));
+        __builtin_amdgcn_s_barrier();
+        __asm__ __volatile__("" ::: "memory");
     };
 
-    u32x4_t ra[A_LD], rb[B_LD];
-    load_global(0, ra, rb);
-    store_lds(0, ra, rb);
-    __syncthreads();
-    bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        // next step's loads (the last iteration re-reads its own step:
-        // harmless), issued first so they fly during this step's MFMAs
-        load_global(min(kt + 1, nk - 1) * BK, ra, rb);
-        read_frags(cur, 0, a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        // sub-steps 0..2: read the next sub-step's fragments among the MFMAs
-        read_frags(cur, 1, a1, b1);
-        mfmas(a0, b0);
-        interleave_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(cur, 2, a0, b0);
-        mfmas(a1, b1);
-        interleave_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(cur, 3, a1, b1);
-        mfmas(a0, b0);
-        interleave_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        // sub-step 3, with the next stage's LDS writes among its MFMAs
-        mfmas(a1, b1);
-        store_lds(cur ^ 1, ra, rb);
+    // One K step kt from stage X: while the MFMAs of sub-step s - 1 run, the
+    // fragments of sub-step s are read (and, in the first sub-step, the
+    // loads of step kt + NSTAGE - 1 go into the stage read in step kt - 1,
+    // free since the last barrier); then the barrier publishes stage Y (step
+    // kt + 1), whose first fragments are read while the last MFMAs of X run.
+    bf16x8_t fa[2][TM], fb[2][TN];
+    auto step = [&](const uint8_t* X, const uint8_t* Y, uint8_t* Fill, int kt) {
+        issue(Fill, kt + NSTAGE - 1);
 #pragma unroll
-        for (int q = 0; q < A_LD + B_LD; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        for (int sub = 1; sub < KSUB; ++sub) {
+            read_frags(X, sub, fa[sub & 1], fb[sub & 1]);
+            mfmas(fa[(sub - 1) & 1], fb[(sub - 1) & 1]);
+            interleave(sub == 1 ? NLD : 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        barrier();
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+        read_frags(Y, 0, fa[0], fb[0]);  // past the last step: unused
+        mfmas(fa[1], fb[1]);
+        interleave(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int j = 0; j < NSTAGE - 1; ++j) {
+        uint8_t* st = j == 0 ? S0 : j == 1 ? S1 : j == 2 ? S2 : S3;
+        issue(st, k_begin + j);
     }
+    barrier();
+    read_frags(S0, 0, fa[0], fb[0]);
+    for (int kt = k_begin; kt < k_end; kt += NSTAGE) {
+        step(S0, S1, pick<NSTAGE - 1>(S0, S1, S2, S3, S4), kt);
+        step(S1, pick<2 % NSTAGE>(S0, S1, S2, S3, S4), S0, kt + 1);
+        if constexpr (NSTAGE > 2)
+            step(S2, pick<3 % NSTAGE>(S0, S1, S2, S3, S4), S1, kt + 2);
+        if constexpr (NSTAGE > 3)
+            step(S3, pick<4 % NSTAGE>(S0, S1, S2, S3, S4), S2, kt + 3);
+        if constexpr (NSTAGE > 4)
+            step(S4, S0, S3, kt + 4);
+    }
+    // Drain: the loads past the last step are out of range but still write
+    // LDS; wait for them before the stages are reused for staging.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // ---- epilogue -------------------------------------------------------------
     // The MFMAs ran with the weights as the first operand, so the 32x32
@@ -252,9 +318,15 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     constexpr int ES = GATEUP ? 2 : 4;                       // output element bytes
     constexpr int RSTRIDE = OCOLS * ES + 16;                 // LDS row stride (bytes)
     constexpr int SLOT = 32 * RSTRIDE;                       // one wave's staging slot
-    static_assert(WM * WN * SLOT <= 2 * (BM + BN) * BK * 2, "staging fits in the stage LDS");
+    // wave w stages in stage w, or in half of stage w / 2 with two stages
+    static_assert(NW <= NSTAGE ? SLOT <= STAGE_BYTES : (NW <= 2 * NSTAGE && 2 * SLOT <= STAGE_BYTES),
+                  "each wave stages in its own part of the stage buffers");
     __syncthreads();  // every wave is done with the K-loop LDS
-    uint8_t* slot = reinterpret_cast<uint8_t*>(&As[0][0]) + wid * SLOT;
+    uint8_t* slot;
+    if constexpr (NW <= NSTAGE)
+        slot = wid == 0 ? S0 : wid == 1 ? S1 : wid == 2 ? S2 : S3;
+    else
+        slot = (wid < 2 ? S0 : S1) + (wid & 1) * (STAGE_BYTES / 2);
     const int col_w = n0 + wn * OCOLS;  // first output column of this wave
     constexpr int CPR = OCOLS * ES / 16;      // 16-byte chunks per staged row
     constexpr int RPI = kWave / CPR;          // rows per store instruction
@@ -293,32 +365,35 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + r * RSTRIDE + ch * 16);
             if (row < rows && col < N) {
                 uint8_t* out = static_cast<uint8_t*>(Cout) +
-                               ((int64_t)(row0 + row) * N + col) * ES;
+                               ((int64_t)ks * split_stride + (int64_t)(row0 + row) * N + col) * ES;
                 *reinterpret_cast<u32x4_t*>(out) = v;
             }
         }
     }
 }
 
-template <bool GATEUP, int BM, int BN, int WM, int WN>
+template <bool GATEUP, int BK, int NSTAGE>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
-                        int64_t A_rows, int Kdim, int N, void* C, int GM, hipStream_t s) {
-    constexpr int BNO = GATEUP ? BN / 2 : BN;
+                        int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
+                        hipStream_t s) {
+    constexpr int BM = 256, BNO = GATEUP ? 128 : 256;
     const int64_t mslots = A_rows / BM + n;
     const int64_t ntn = (N + BNO - 1) / BNO;
-    int64_t blocks = mslots * ntn;
-    blocks = (blocks + 7) / 8 * 8;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t g1 = (mslots * ntn + 7) / 8 * 8;
+    const int64_t blocks = g1 * splits;
+    if (blocks > 0x7fffffff || splits < 1 || (GATEUP && splits != 1))
+        return hipErrorInvalidConfiguration;
     const bool ktail = Kdim % BK != 0;
+    const int64_t stride = A_rows * (int64_t)N;
     if (ktail)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, BM, BN, WM, WN>), dim3((unsigned)blocks),
-                           dim3(WM * WN * kWave), 0, s, A, A_src_rows, perm, K, B1, B3, offsets,
-                           n, Kdim, N, C, (int)mslots, GM);
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, BK, NSTAGE>), dim3((unsigned)blocks),
+                           dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
+                           C, (int)mslots, GM, splits, stride);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, BM, BN, WM, WN>),
-                           dim3((unsigned)blocks), dim3(WM * WN * kWave), 0, s, A, A_src_rows,
-                           perm, K, B1, B3, offsets, n, Kdim, N, C, (int)mslots, GM);
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, BK, NSTAGE>), dim3((unsigned)blocks),
+                           dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
+                           C, (int)mslots, GM, splits, stride);
     return hipGetLastError();
 }
 
@@ -330,17 +405,31 @@ bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N) {
     return A_src_rows * Kdim * 2 < lim && N * Kdim * 2 < lim;
 }
 
+int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_splits) {
+    // Expected tiles: every expert's last row tile is half full on average.
+    const int64_t mt = (A_rows + 255) / 256 + n / 2;
+    const int64_t tiles = mt * ((N + 255) / 256);
+    const int64_t rem = tiles % cus;
+    // A last round at most half full runs twice as many half-length tiles
+    // instead.
+    if (max_splits >= 2 && rem != 0 && rem * 2 <= cus && Kdim >= 64) return 2;
+    return 1;
+}
+
 hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                   const int32_t* perm, int K, const uint16_t* B1,
                                   const uint16_t* B3, const int32_t* offsets, int n,
-                                  int64_t A_rows, int Kdim, int N, void* C, hipStream_t s) {
+                                  int64_t A_rows, int Kdim, int N, void* C, int splits,
+                                  hipStream_t s) {
     if (!tiled_fits(A_src_rows, Kdim, N)) return hipErrorInvalidValue;
-    const int GM = 4;
+    // 64-deep K steps (128-byte row slices per load) in two stages: measured
+    // faster on random operands than 32-deep steps in four or five stages.
+    const int GM = 8;
     if (gateup)
-        return launch_tiled<true, 256, 256, 2, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n,
-                                                  A_rows, Kdim, N, C, GM, s);
-    return launch_tiled<false, 256, 256, 2, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n,
-                                               A_rows, Kdim, N, C, GM, s);
+        return launch_tiled<true, 64, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows,
+                                         Kdim, N, C, GM, 1, s);
+    return launch_tiled<false, 64, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim,
+                                      N, C, GM, splits, s);
 }
 
 }  // namespace moe

@@ -22,10 +22,17 @@ hipError_t launch_gemm_f32(bool gateup, const float* A, const int32_t* perm, int
 
 // bf16 MFMA grouped GEMMs, LDS-tiled (many rows per expert).  A has
 // A_src_rows rows of Kdim elements (x, u or H).
+// The down projection (gateup false) may split K into `splits` partial sums,
+// written `A_rows * N` elements apart; gate/up takes splits = 1.
 hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                   const int32_t* perm, int K, const uint16_t* B1,
                                   const uint16_t* B3, const int32_t* offsets, int n,
-                                  int64_t A_rows, int Kdim, int N, void* C, hipStream_t s);
+                                  int64_t A_rows, int Kdim, int N, void* C, int splits,
+                                  hipStream_t s);
+// K splits worth using for the tiled down projection on `cus` compute units
+// (at most max_splits): 2 when the last round of tiles would be at most half
+// full, else 1.  Depends on sizes only.
+int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_splits);
 // Whether the tiled kernels can take these sizes (32-bit buffer offsets).
 bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N);
 
