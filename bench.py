@@ -141,6 +141,79 @@ def traffic_for(workload: str, src_sha: str):
     return t.get("bytes_per_launch")
 
 
+# Substrings naming the gate/up kernel in a rocprofv3 counter file, and the
+# plain copy kernel of the calibration run.
+GATE_UP_KERNEL = {"skinny": "gemm_skinny_kernel<true", "tiled": "gemm_bf16_kernel<true"}
+COPY_KERNEL = "copy"
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES, five times: the reference kernel
+    whose FETCH_SIZE / WRITE_SIZE counters scale the gate/up kernel's."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _counter_mean_kib(csv_path: str, counter: str, name_part: str) -> float:
+    """Mean over the matching dispatches (first one skipped when there are
+    several) of a rocprofv3 derived counter, in KiB per dispatch."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    names = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+                continue
+            k = int(r["Dispatch_Id"])
+            per[k] += float(r["Counter_Value"])
+            names[k] = r["Kernel_Name"]
+    ks = sorted(per)
+    if not ks:
+        raise SystemExit(f"no {counter} for a kernel named *{name_part}* in {csv_path}")
+    if len(ks) > 1:
+        ks = ks[1:]
+    return sum(per[k] for k in ks) / len(ks)
+
+
+def write_traffic(workload: str, dirs, command: str):
+    """profiles/traffic.json[workload] from four rocprofv3 --pmc runs: the
+    bench's FETCH_SIZE and WRITE_SIZE, then the copy calibration's."""
+    from sparse_mixture_experts_14_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    skinny = w.dtype == "bf16" and w.T * w.K <= 16 * w.n
+    part = GATE_UP_KERNEL["skinny" if skinny else "tiled"]
+    f_k, w_k, cf_k, cw_k = (os.path.join(d, "run_counter_collection.csv") for d in dirs)
+    fetch = _counter_mean_kib(f_k, "FETCH_SIZE", part) * 1024
+    write = _counter_mean_kib(w_k, "WRITE_SIZE", part) * 1024
+    cfetch = _counter_mean_kib(cf_k, "FETCH_SIZE", COPY_KERNEL) * 1024
+    cwrite = _counter_mean_kib(cw_k, "WRITE_SIZE", COPY_KERNEL) * 1024
+    fs, ws = COPY_BYTES / cfetch, COPY_BYTES / cwrite
+    _, src = dominant_kernel(w, skinny)
+    entry = {"source_sha": kernel_source_sha(src), "kernel": part,
+             "bytes_per_launch": round(fetch * fs + write * ws),
+             "fetch_bytes_raw": round(fetch), "write_bytes_raw": round(write),
+             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+             "copy_kernel_bytes": COPY_BYTES, "command": command}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: entry}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,7 +223,21 @@ def main():
                     choices=["tiny", "decode", "prefill", "skew", "stack"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the plain copy that calibrates the traffic counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
+                    help="rocprofv3 --pmc output dirs (bench FETCH_SIZE, bench WRITE_SIZE, "
+                         "copy FETCH_SIZE, copy WRITE_SIZE): write profiles/traffic.json "
+                         "for --workload and exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="command line recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.workload, args.traffic_from, args.traffic_command)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer is built and timed on a single MI355X; "
               "run it with --gpus 1", file=sys.stderr)
