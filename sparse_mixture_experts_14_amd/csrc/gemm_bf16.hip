@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
-                      int n, int Kdim, int N, void* __restrict__ Cout, int mslots, int GM,
-                      int splits, int64_t split_stride) {
+                      int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
+                      int64_t split_stride) {
     constexpr int BM = 256, BN = 256, WM = 2, WN = 2, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (accumulator space)
     constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 MFMA tiles per wave
@@ -93,23 +93,41 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     __shared__ __attribute__((aligned(1024))) uint8_t S4[NSTAGE > 4 ? STAGE_BYTES : 16];
 
     // ---- tile coordinates -------------------------------------------------
-    const int G = gridDim.x;  // splits x G1, G1 a multiple of 8
-    const int b = blockIdx.x;
-    const int L0 = (b & 7) * (G >> 3) + (b >> 3);
-    const int G1 = G / splits;
-    const int ks = L0 / G1;  // K split of this block
-    const int L = L0 - ks * G1;
+    // The real tiles (every expert's row tiles times the column tiles, per K
+    // split) are known only here, from the expert offsets; the grid is an
+    // upper bound and blocks past the real tiles exit.  Block b runs on XCD
+    // b % 8, and each XCD takes one contiguous eighth of the real tiles in
+    // (split, expert, row group, column, row) order, so the 32 tiles its CUs
+    // run together share token and weight tiles in its L2 and every XCD gets
+    // the same number of tiles.  Inside an expert the row tiles go in groups
+    // of GM: the row tile varies fastest, so a weight tile is fetched once
+    // for the group.
     const int ntiles_n = (N + BNO - 1) / BNO;
+    int mt_total = 0;
+    for (int q = 0; q < n; ++q) mt_total += (offsets[q + 1] - offsets[q] + BM - 1) / BM;
+    const int tiles = mt_total * ntiles_n;
+    const int per_xcd = (tiles * splits + 7) / 8;
+    const int jx = (int)(blockIdx.x >> 3);
+    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
+    if (jx >= per_xcd || L0 >= tiles * splits) return;
+    const int ks = L0 / tiles;  // K split of this block
+    int L = L0 - ks * tiles;
+    int e = 0, start = offsets[0];
+    for (;; ++e) {  // ends: L < tiles
+        const int cnt = (offsets[e + 1] - start + BM - 1) / BM * ntiles_n;
+        if (L < cnt) break;
+        L -= cnt;
+        start = offsets[e + 1];
+    }
+    const int end = offsets[e + 1];
+    const int te = (end - start + BM - 1) / BM;  // row tiles of expert e
     const int group = L / (GM * ntiles_n);
-    const int first_m = group * GM;
-    if (first_m >= mslots) return;
-    const int gm = min(GM, mslots - first_m);
+    const int gm = min(GM, te - group * GM);
     const int local = L - group * GM * ntiles_n;
-    const int mt = first_m + local % gm;
+    const int mt = group * GM + local % gm;
     const int nt = local / gm;
-    if (nt >= ntiles_n) return;  // padding block of the last group
-    int e, row0, rows;
-    if (!locate_tile<BM>(offsets, n, mt, e, row0, rows)) return;
+    const int row0 = start + mt * BM;
+    const int rows = min(BM, end - row0);
     const int n0 = nt * BNO;
 
     const int tid = threadIdx.x;
@@ -378,10 +396,10 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
                         hipStream_t s) {
     constexpr int BM = 256, BNO = GATEUP ? 128 : 256;
+    // upper bound of the row tiles: each expert's last one may be partial
     const int64_t mslots = A_rows / BM + n;
     const int64_t ntn = (N + BNO - 1) / BNO;
-    const int64_t g1 = (mslots * ntn + 7) / 8 * 8;
-    const int64_t blocks = g1 * splits;
+    const int64_t blocks = (mslots * ntn * splits + 7) / 8 * 8;
     if (blocks > 0x7fffffff || splits < 1 || (GATEUP && splits != 1))
         return hipErrorInvalidConfiguration;
     const bool ktail = Kdim % BK != 0;
@@ -389,11 +407,11 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     if (ktail)
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, BK, NSTAGE>), dim3((unsigned)blocks),
                            dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
-                           C, (int)mslots, GM, splits, stride);
+                           C, GM, splits, stride);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, BK, NSTAGE>), dim3((unsigned)blocks),
                            dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
-                           C, (int)mslots, GM, splits, stride);
+                           C, GM, splits, stride);
     return hipGetLastError();
 }
 
