@@ -7,40 +7,56 @@
 // summary ("Implementasi dan Efisiensi Inferensi") describes running all
 // experts as one grouped product over an uneven number of tokens per expert;
 // here the rows of every expert are contiguous after the permutation stage
-// and a workgroup owns one 256 x 256 tile of one expert.
+// and a workgroup owns one output tile of one expert.
 //
 //   gate/up:  H[p][f] = bf16( SiLU(u_p . W1_e[f]) * (u_p . W3_e[f]) )
 //             A rows are gathered, u_p = x[perm[p] / K]; the B tile holds
-//             128 rows of W1 and the same 128 rows of W3, so the SiLU*mul
-//             epilogue finds both accumulators in the same lane.
+//             W1 rows and the same W3 rows, so the SiLU*mul epilogue finds
+//             both accumulators in the same lane.
 //   down:     O[s][p][c] = sum over the K range of split s of H_p . W2_e[c]
 //             (fp32 partial sums; the combine stage adds the splits).
 //
-// Tile shape.  256 x 256 accumulator tile, 4 waves, each 128 x 128 (4 x 4
-// MFMA tiles of 32 x 32, 256 fp32 accumulators per lane, in AGPRs): per
-// 16-element K sub-step a wave reads 4 A and 4 B fragments from LDS for 16
-// MFMAs.  Both operands are K-contiguous ([out][in] weights), which is the
-// per-lane 8-element K run each MFMA operand wants.  The weights are the
-// MFMA's first operand, so a lane ends up owning 4 contiguous output columns.
+// Tile shapes.  Four waves, each holding a 128 x 128 fp32 accumulator (4 x 4
+// MFMA tiles of 32 x 32, 256 accumulators per lane, in AGPRs); per 16-deep K
+// sub-step a wave reads 4 A and 4 B fragments from LDS for 16 MFMAs.  A
+// workgroup owns 256 token rows x 256 B rows (waves 2 x 2), or -- for an
+// expert's last gate/up row tile when it has at most 128 rows -- 128 token
+// rows x 512 B rows (waves 1 x 4), the same MFMA work over twice the
+// columns, so a short tail costs half a tile instead of a whole one.  Both operands are
+// K-contiguous ([out][in] weights), the per-lane 8-element K run each MFMA
+// operand wants; the weights are the MFMA's first operand, so a lane ends up
+// owning 4 contiguous output columns.
 //
-// Pipeline.  NSTAGE LDS stages of BK-deep A and B tiles.  Each stage is filled
-// by buffer loads with the LDS flag (global -> LDS, no registers, no LDS
-// write instructions), issued NSTAGE - 1 steps ahead; one barrier per K step
-// waits only for the loads of the next step.  LDS rows are BK bf16 with the
-// 16-byte chunk XOR-swizzled so that the fragment reads of 16 consecutive
-// rows hit distinct banks.  Rows past the tile are clamped to a valid row
-// (never stored); a K tail and the padded steps past the end load through an
-// out-of-range offset, which writes zeros.
-//
-// Tile order: the 1-D grid is first spread over the 8 XCDs (block b runs on
-// XCD b % 8, so consecutive logical tiles go to one XCD and share its L2),
-// then walked in groups of GM row tiles: inside a group the row tile varies
-// fastest, so a weight tile is fetched once for GM row tiles.
+// Pipeline.  Two LDS stages of 64-deep A and B tiles (rows of 128 bytes, the
+// 16-byte chunk XOR-swizzled by (row / 2) % 8 so that the fragment reads of
+// 16 consecutive rows hit distinct banks).  A stage is filled by buffer loads
+// with the LDS flag (global -> LDS, no registers, no LDS write instructions),
+// issued one step ahead during the first MFMAs of a step; one barrier per
+// step waits for them.  Rows past the tile are clamped to a valid row (never
+// stored); a K tail and the step past the end load through an out-of-range
+// offset, which writes zeros.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
+
+constexpr int BK = 64;              // K per step
+constexpr int ROW_BYTES = BK * 2;   // one LDS row
+constexpr int CH = ROW_BYTES / 16;  // 16-byte chunks per row
+constexpr int RPB = 256 / ROW_BYTES;  // rows per 256-byte bank sweep
+constexpr int KSUB = BK / 16;       // MFMA sub-steps per K step
+constexpr int ROWS_LD = 1024 / ROW_BYTES;  // LDS rows per load instruction
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Shape {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+};
+using Square = Shape<256, 256, 2, 2>;  // full row tiles
+using Wide = Shape<128, 512, 1, 4>;    // an expert's last row tile of <= 128 rows
+constexpr int STAGE_MAX =
+    Square::STAGE_BYTES > Wide::STAGE_BYTES ? Square::STAGE_BYTES : Wide::STAGE_BYTES;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
@@ -54,82 +70,33 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
-template <int J>
-__device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
-                                         uint8_t* s4) {
-    if constexpr (J == 0) return s0;
-    if constexpr (J == 1) return s1;
-    if constexpr (J == 2) return s2;
-    if constexpr (J == 3) return s3;
-    return s4;
-}
+struct TileArgs {
+    const uint16_t* A;
+    int64_t A_src_rows;
+    const int32_t* perm;
+    int K;
+    const uint16_t* B1;  // this expert's weights
+    const uint16_t* B3;
+    int Kdim, N;
+    void* Cout;           // already offset to this split's partial sums
+    int row0, rows, n0;   // tile rows [row0, row0 + rows), first output column
+    int k_begin, k_end;   // K steps of this split
+};
 
-template <bool GATEUP, bool KTAIL, int BK, int NSTAGE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
-                      const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
-                      const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
-                      int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
-                      int64_t split_stride) {
-    constexpr int BM = 256, BN = 256, WM = 2, WN = 2, NW = WM * WN;
+// One output tile: loads, MFMA main loop and epilogue.  S0 and S1 are the two
+// LDS stages (separate objects, so the compiler can tell the stage being read
+// from the stage being filled).
+template <bool GATEUP, bool KTAIL, class SH, int STG>
+__device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_t* S1) {
+    constexpr int BM = SH::BM, BN = SH::BN, WM = SH::WM, WN = SH::WN, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (accumulator space)
     constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 MFMA tiles per wave
-    constexpr int BNO = GATEUP ? BN / 2 : BN;     // output columns per tile
-    constexpr int KSUB = BK / 16;                 // MFMA sub-steps per K step
-    constexpr int ROW_BYTES = BK * 2;             // one LDS row: BK bf16
-    constexpr int CH = ROW_BYTES / 16;            // 16-byte chunks per row
-    constexpr int RPB = 256 / ROW_BYTES;          // rows per 256-byte bank sweep
     constexpr int A_BYTES = BM * ROW_BYTES;       // A tile of one stage
-    constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-    static_assert(KSUB % 2 == 0 && NSTAGE >= 2 && NSTAGE <= 5, "pipeline shape");
-    static_assert(!GATEUP || (TN % 2 == 0), "gate/up needs W1 and W3 tiles in pairs");
+    constexpr int STAGE_BYTES = SH::STAGE_BYTES;
+    static_assert(NW == 4 && TM == 4 && TN == 4, "four waves of 128 x 128");
+    static_assert(STAGE_BYTES <= STG, "stage fits (STG: bytes of each stage object)");
 
-    // One object per stage (A tile, then B tile), so that the compiler can
-    // tell the stage being read from the stages being filled.
-    __shared__ __attribute__((aligned(1024))) uint8_t S0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t S1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t S2[NSTAGE > 2 ? STAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t S3[NSTAGE > 3 ? STAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t S4[NSTAGE > 4 ? STAGE_BYTES : 16];
-
-    // ---- tile coordinates -------------------------------------------------
-    // The real tiles (every expert's row tiles times the column tiles, per K
-    // split) are known only here, from the expert offsets; the grid is an
-    // upper bound and blocks past the real tiles exit.  Block b runs on XCD
-    // b % 8, and each XCD takes one contiguous eighth of the real tiles in
-    // (split, expert, row group, column, row) order, so the 32 tiles its CUs
-    // run together share token and weight tiles in its L2 and every XCD gets
-    // the same number of tiles.  Inside an expert the row tiles go in groups
-    // of GM: the row tile varies fastest, so a weight tile is fetched once
-    // for the group.
-    const int ntiles_n = (N + BNO - 1) / BNO;
-    int mt_total = 0;
-    for (int q = 0; q < n; ++q) mt_total += (offsets[q + 1] - offsets[q] + BM - 1) / BM;
-    const int tiles = mt_total * ntiles_n;
-    const int per_xcd = (tiles * splits + 7) / 8;
-    const int jx = (int)(blockIdx.x >> 3);
-    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
-    if (jx >= per_xcd || L0 >= tiles * splits) return;
-    const int ks = L0 / tiles;  // K split of this block
-    int L = L0 - ks * tiles;
-    int e = 0, start = offsets[0];
-    for (;; ++e) {  // ends: L < tiles
-        const int cnt = (offsets[e + 1] - start + BM - 1) / BM * ntiles_n;
-        if (L < cnt) break;
-        L -= cnt;
-        start = offsets[e + 1];
-    }
-    const int end = offsets[e + 1];
-    const int te = (end - start + BM - 1) / BM;  // row tiles of expert e
-    const int group = L / (GM * ntiles_n);
-    const int gm = min(GM, te - group * GM);
-    const int local = L - group * GM * ntiles_n;
-    const int mt = group * GM + local % gm;
-    const int nt = local / gm;
-    const int row0 = start + mt * BM;
-    const int rows = min(BM, end - row0);
-    const int n0 = nt * BNO;
-
+    const int Kdim = t.Kdim, N = t.N, rows = t.rows, n0 = t.n0;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -140,22 +107,20 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // M0 + 16 l, so one instruction fills 1 KB = ROWS_LD consecutive LDS rows.
     // Lane l serves row ROWS_LD q + l / CH and physical chunk l % CH, i.e. the
     // logical chunk (l % CH) ^ swizzle(row): it fetches exactly the 16 bytes
-    // that belong there, and the CH lanes of a row together read its K slice.
-    // Each wave issues A_LD + B_LD such loads per K step.
-    constexpr int ROWS_LD = 1024 / ROW_BYTES;          // rows per load instruction
-    constexpr int A_LD = BM / ROWS_LD / NW;            // A loads per wave per K step
+    // that belong there, and the CH lanes of a row together read its 128-byte
+    // K slice.  Each wave issues A_LD + B_LD such loads per K step.
+    constexpr int A_LD = BM / ROWS_LD / NW;  // A loads per wave per K step
     constexpr int B_LD = BN / ROWS_LD / NW;
     constexpr int NLD = A_LD + B_LD;
     static_assert(A_LD * ROWS_LD * NW == BM && B_LD * ROWS_LD * NW == BN, "loader split");
     static_assert(!GATEUP || B_LD % 2 == 0, "W1 and W3 halves of the B tile");
-    static_assert(NLD <= TM * TN, "loads fit between the first sub-step's MFMAs");
     const int rr = lane / CH, pc = lane % CH;
     const uint32_t src_row_bytes = (uint32_t)Kdim * 2u;
-    const __amdgpu_buffer_rsrc_t a_rs = rsrc(A, A_src_rows * (int64_t)Kdim * 2);
+    const __amdgpu_buffer_rsrc_t a_rs = rsrc(t.A, t.A_src_rows * (int64_t)Kdim * 2);
     const int64_t wbytes = (int64_t)N * Kdim * 2;
-    const __amdgpu_buffer_rsrc_t b1_rs = rsrc(B1 + (int64_t)e * N * Kdim, wbytes);
-    const __amdgpu_buffer_rsrc_t b3_rs = GATEUP ? rsrc(B3 + (int64_t)e * N * Kdim, wbytes) : b1_rs;
-    const __amdgpu_buffer_rsrc_t null_rs = rsrc(A, 0);
+    const __amdgpu_buffer_rsrc_t b1_rs = rsrc(t.B1, wbytes);
+    const __amdgpu_buffer_rsrc_t b3_rs = GATEUP ? rsrc(t.B3, wbytes) : b1_rs;
+    const __amdgpu_buffer_rsrc_t null_rs = rsrc(t.A, 0);
     // first LDS row of load i (A, B)
     auto a_lrow = [&](int i) { return (wid * A_LD + i) * ROWS_LD; };
     auto b_lrow = [&](int i) {
@@ -169,8 +134,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     for (int i = 0; i < A_LD; ++i) {
         const int r = a_lrow(i) + rr;
         const int c = pc ^ ((r / RPB) % CH);
-        const int p = row0 + min(r, rows - 1);  // rows past the tile: a valid row, never stored
-        const uint32_t src = GATEUP ? (uint32_t)(perm[p] / K) : (uint32_t)p;
+        const int p = t.row0 + min(r, rows - 1);  // rows past the tile: a valid row, never stored
+        const uint32_t src = GATEUP ? (uint32_t)(t.perm[p] / t.K) : (uint32_t)p;
         a_off[i] = src * src_row_bytes + (uint32_t)c * 16u;
         a_k8[i] = c * 8;
     }
@@ -182,15 +147,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         b_off[i] = (uint32_t)min(col, N - 1) * src_row_bytes + (uint32_t)c * 16u;
         b_k8[i] = c * 8;
     }
-    // K steps [k_begin, k_end) of this split
-    const int nk_all = (Kdim + BK - 1) / BK;
-    const int per_split = (nk_all + splits - 1) / splits;
-    const int k_begin = min(nk_all, ks * per_split);
-    const int k_end = min(nk_all, k_begin + per_split);
-    // Loads of K step kt into stage `st`.  Steps past the end go through a
+    const int k_end = t.k_end;
+    // Loads of K step kt into stage `st`.  A step past the end goes through a
     // zero-size resource: every load is out of range and writes zeros, so the
-    // step count can be padded to a multiple of NSTAGE with exact results and
-    // an unchanged load count.  K tails: chunks past Kdim are out of range.
+    // issue pattern and the load count stay the same.  K tails: chunks past
+    // Kdim get an out-of-range offset.
     auto issue = [&](uint8_t* st, int kt) {
         const bool live = kt < k_end;
         const int k0 = live ? kt * BK : 0;
@@ -262,32 +223,35 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // Scheduling hints (group masks: 0x008 MFMA, 0x020 VMEM read, 0x100 LDS
     // read): the LDS reads of the next sub-step go out one per MFMA at the
     // start of a sub-step, so their latency hides behind the remaining MFMAs;
-    // the first sub-step of a step also carries the loads of a later step.
+    // the first sub-step of a step also carries the next step's loads (LPM
+    // per MFMA).
     auto interleave = [&](int nloads) {
+        constexpr int LPM = (NLD + TM * TN - 1) / (TM * TN);
 #pragma unroll
         for (int q = 0; q < TM * TN; ++q) {
             if (q < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (q < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+            for (int r = 0; r < LPM; ++r)
+                if (q * LPM + r < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     };
-    // Block-wide barrier that only waits for this wave's loads of the step
-    // about to be read (the NSTAGE - 2 later steps' loads stay in flight) and
-    // for its own LDS reads (the stage they read is refilled after it).
+    // Block-wide barrier that waits for this wave's loads (the step about to
+    // be read) and its own LDS reads (the stage they read is refilled next).
     auto barrier = [&]() {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NSTAGE - 2) * NLD, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __builtin_amdgcn_s_barrier();
         __asm__ __volatile__("" ::: "memory");
     };
 
     // One K step kt from stage X: while the MFMAs of sub-step s - 1 run, the
     // fragments of sub-step s are read (and, in the first sub-step, the
-    // loads of step kt + NSTAGE - 1 go into the stage read in step kt - 1,
-    // free since the last barrier); then the barrier publishes stage Y (step
-    // kt + 1), whose first fragments are read while the last MFMAs of X run.
+    // loads of step kt + 1 go into stage Y, free since the last barrier);
+    // then the barrier publishes Y, whose first fragments are read while the
+    // last MFMAs of X run.
     bf16x8_t fa[2][TM], fb[2][TN];
-    auto step = [&](const uint8_t* X, const uint8_t* Y, uint8_t* Fill, int kt) {
-        issue(Fill, kt + NSTAGE - 1);
+    auto step = [&](const uint8_t* X, uint8_t* Y, int kt) {
+        issue(Y, kt + 1);
 #pragma unroll
         for (int sub = 1; sub < KSUB; ++sub) {
             read_frags(X, sub, fa[sub & 1], fb[sub & 1]);
@@ -303,22 +267,12 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         __builtin_amdgcn_sched_barrier(0);
     };
 
-#pragma unroll
-    for (int j = 0; j < NSTAGE - 1; ++j) {
-        uint8_t* st = j == 0 ? S0 : j == 1 ? S1 : j == 2 ? S2 : S3;
-        issue(st, k_begin + j);
-    }
+    issue(S0, t.k_begin);
     barrier();
     read_frags(S0, 0, fa[0], fb[0]);
-    for (int kt = k_begin; kt < k_end; kt += NSTAGE) {
-        step(S0, S1, pick<NSTAGE - 1>(S0, S1, S2, S3, S4), kt);
-        step(S1, pick<2 % NSTAGE>(S0, S1, S2, S3, S4), S0, kt + 1);
-        if constexpr (NSTAGE > 2)
-            step(S2, pick<3 % NSTAGE>(S0, S1, S2, S3, S4), S1, kt + 2);
-        if constexpr (NSTAGE > 3)
-            step(S3, pick<4 % NSTAGE>(S0, S1, S2, S3, S4), S2, kt + 3);
-        if constexpr (NSTAGE > 4)
-            step(S4, S0, S3, kt + 4);
+    for (int kt = t.k_begin; kt < k_end; kt += 2) {
+        step(S0, S1, kt);
+        step(S1, S0, kt + 1);
     }
     // Drain: the loads past the last step are out of range but still write
     // LDS; wait for them before the stages are reused for staging.
@@ -336,15 +290,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     constexpr int ES = GATEUP ? 2 : 4;                       // output element bytes
     constexpr int RSTRIDE = OCOLS * ES + 16;                 // LDS row stride (bytes)
     constexpr int SLOT = 32 * RSTRIDE;                       // one wave's staging slot
-    // wave w stages in stage w, or in half of stage w / 2 with two stages
-    static_assert(NW <= NSTAGE ? SLOT <= STAGE_BYTES : (NW <= 2 * NSTAGE && 2 * SLOT <= STAGE_BYTES),
-                  "each wave stages in its own part of the stage buffers");
+    static_assert(2 * SLOT <= STG, "wave w stages in half of stage w / 2");
     __syncthreads();  // every wave is done with the K-loop LDS
-    uint8_t* slot;
-    if constexpr (NW <= NSTAGE)
-        slot = wid == 0 ? S0 : wid == 1 ? S1 : wid == 2 ? S2 : S3;
-    else
-        slot = (wid < 2 ? S0 : S1) + (wid & 1) * (STAGE_BYTES / 2);
+    uint8_t* slot = (wid < 2 ? S0 : S1) + (wid & 1) * (STG / 2);
     const int col_w = n0 + wn * OCOLS;  // first output column of this wave
     constexpr int CPR = OCOLS * ES / 16;      // 16-byte chunks per staged row
     constexpr int RPI = kWave / CPR;          // rows per store instruction
@@ -376,28 +324,125 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         // write back: lane -> (row, 16-byte chunk).  The slot is the wave's own
         // and LDS operations of one wave complete in order: no barrier needed.
 #pragma unroll
-        for (int rr = 0; rr < 32; rr += RPI) {
-            const int r = rr + lane / CPR, ch = lane % CPR;
+        for (int rr2 = 0; rr2 < 32; rr2 += RPI) {
+            const int r = rr2 + lane / CPR, ch = lane % CPR;
             const int row = wm * WTM + i * 32 + r;
             const int col = col_w + ch * (16 / ES);
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + r * RSTRIDE + ch * 16);
             if (row < rows && col < N) {
-                uint8_t* out = static_cast<uint8_t*>(Cout) +
-                               ((int64_t)ks * split_stride + (int64_t)(row0 + row) * N + col) * ES;
+                uint8_t* out = static_cast<uint8_t*>(t.Cout) +
+                               ((int64_t)(t.row0 + row) * N + col) * ES;
                 *reinterpret_cast<u32x4_t*>(out) = v;
             }
         }
     }
 }
 
-template <bool GATEUP, int BK, int NSTAGE>
+template <bool GATEUP, bool KTAIL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
+                      const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
+                      const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
+                      int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
+                      int64_t split_stride) {
+    // gate/up also runs wide tiles (larger stages)
+    constexpr int STG = GATEUP ? STAGE_MAX : Square::STAGE_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t S0[STG];
+    __shared__ __attribute__((aligned(1024))) uint8_t S1[STG];
+
+    // ---- tile coordinates -------------------------------------------------
+    // Expert e with m rows has m / 256 full row tiles; a remainder of more
+    // than 128 rows is one more (partial) square row tile, one of at most 128
+    // rows a wide row tile.  The real tiles (per K split) are known only here,
+    // from the expert offsets; the grid is an upper bound and blocks past the
+    // real tiles exit.  Block b runs on XCD b % 8, and each XCD takes one
+    // contiguous eighth of the real tiles, so every XCD gets the same number
+    // of tiles and the 32 tiles its CUs run together are neighbours in the
+    // order below, sharing token and weight tiles in its L2.
+    //
+    // Order: split, expert, row group (GM square row tiles; the wide row tile
+    // joins the last group), column pair, then inside a column pair the
+    // group's square tiles of both columns followed by the wide tile that
+    // spans them -- all tiles reading one weight panel run back to back.
+    constexpr int BNO_S = GATEUP ? Square::BN / 2 : Square::BN;  // output columns per tile
+    const int ntn_s = (N + BNO_S - 1) / BNO_S;  // square column tiles
+    const int npair = (ntn_s + 1) / 2;           // column pairs = wide column tiles
+    // Wide tail tiles pay off for gate/up; for the down projection (fewer,
+    // longer tiles) they measured slower, so its tails stay square.
+    constexpr int WIDE_MAX = GATEUP ? Wide::BM : 0;
+    auto expert_tiles = [&](int m, int& nsq, int& nwide) {
+        const int rem = m % Square::BM;
+        nsq = m / Square::BM + (rem > WIDE_MAX ? 1 : 0);
+        nwide = rem > 0 && rem <= WIDE_MAX ? 1 : 0;
+        return nsq * ntn_s + nwide * npair;
+    };
+    int tiles = 0;
+    for (int q = 0; q < n; ++q) {
+        int a, c;
+        tiles += expert_tiles(offsets[q + 1] - offsets[q], a, c);
+    }
+    const int per_xcd = (tiles * splits + 7) / 8;
+    const int jx = (int)(blockIdx.x >> 3);
+    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
+    if (jx >= per_xcd || L0 >= tiles * splits) return;
+    const int ks = L0 / tiles;  // K split of this block
+    int L = L0 - ks * tiles;
+    int e = 0, start = offsets[0], nsq = 0, nwide = 0;
+    for (;; ++e) {  // ends: L < tiles
+        const int cnt = expert_tiles(offsets[e + 1] - start, nsq, nwide);
+        if (L < cnt) break;
+        L -= cnt;
+        start = offsets[e + 1];
+    }
+    const int end = offsets[e + 1];
+    // row group: all but the last hold GM square row tiles and no wide tile
+    const int ngroups = max(1, (nsq + GM - 1) / GM);
+    int g = min(L / (GM * ntn_s), ngroups - 1);
+    L -= g * GM * ntn_s;
+    const int gm = min(GM, nsq - g * GM);  // square row tiles of this group (may be 0)
+    const int w = g == ngroups - 1 ? nwide : 0;
+    // column pair: 2 gm + w tiles (gm + w in a last, single-column pair)
+    const int c = min(L / (2 * gm + w), npair - 1);
+    L -= c * (2 * gm + w);
+    const int ncol = min(2, ntn_s - 2 * c);  // square columns in this pair
+
+    TileArgs t;
+    t.A = A;
+    t.A_src_rows = A_src_rows;
+    t.perm = perm;
+    t.K = K;
+    t.B1 = B1 + (int64_t)e * N * Kdim;
+    t.B3 = GATEUP ? B3 + (int64_t)e * N * Kdim : nullptr;
+    t.Kdim = Kdim;
+    t.N = N;
+    t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP ? 2 : 4);
+    const int nk_all = (Kdim + BK - 1) / BK;
+    const int per_split = (nk_all + splits - 1) / splits;
+    t.k_begin = min(nk_all, ks * per_split);
+    t.k_end = min(nk_all, t.k_begin + per_split);
+    if (L < gm * ncol) {
+        const int mt = g * GM + L % gm;
+        t.row0 = start + mt * Square::BM;
+        t.rows = min(Square::BM, end - t.row0);
+        t.n0 = (2 * c + L / gm) * BNO_S;
+        tile_body<GATEUP, KTAIL, Square, STG>(t, S0, S1);
+    } else if constexpr (WIDE_MAX > 0) {
+        t.row0 = start + nsq * Square::BM;
+        t.rows = end - t.row0;
+        t.n0 = 2 * c * BNO_S;
+        tile_body<GATEUP, KTAIL, Wide, STG>(t, S0, S1);
+    }
+}
+
+template <bool GATEUP>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
                         hipStream_t s) {
-    constexpr int BM = 256, BNO = GATEUP ? 128 : 256;
-    // upper bound of the row tiles: each expert's last one may be partial
-    const int64_t mslots = A_rows / BM + n;
+    constexpr int BNO = GATEUP ? Square::BN / 2 : Square::BN;
+    // upper bound of the tiles: each expert's last row tile may be partial
+    // (a wide tile never has more column tiles than a square one)
+    const int64_t mslots = A_rows / Square::BM + n;
     const int64_t ntn = (N + BNO - 1) / BNO;
     const int64_t blocks = (mslots * ntn * splits + 7) / 8 * 8;
     if (blocks > 0x7fffffff || splits < 1 || (GATEUP && splits != 1))
@@ -405,13 +450,13 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     const bool ktail = Kdim % BK != 0;
     const int64_t stride = A_rows * (int64_t)N;
     if (ktail)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, BK, NSTAGE>), dim3((unsigned)blocks),
-                           dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
-                           C, GM, splits, stride);
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N, C, GM, splits,
+                           stride);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, BK, NSTAGE>), dim3((unsigned)blocks),
-                           dim3(256), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N,
-                           C, GM, splits, stride);
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false>), dim3((unsigned)blocks), dim3(256),
+                           0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim, N, C, GM,
+                           splits, stride);
     return hipGetLastError();
 }
 
@@ -440,14 +485,12 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
                                   hipStream_t s) {
     if (!tiled_fits(A_src_rows, Kdim, N)) return hipErrorInvalidValue;
-    // 64-deep K steps (128-byte row slices per load) in two stages: measured
-    // faster on random operands than 32-deep steps in four or five stages.
     const int GM = 8;
     if (gateup)
-        return launch_tiled<true, 64, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows,
-                                         Kdim, N, C, GM, 1, s);
-    return launch_tiled<false, 64, 2>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim,
-                                      N, C, GM, splits, s);
+        return launch_tiled<true>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
+                                  C, GM, 1, s);
+    return launch_tiled<false>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N, C,
+                               GM, splits, s);
 }
 
 }  // namespace moe
