@@ -188,6 +188,174 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
 }
 
+// Resident-weight variant (bf16, n = 8, d = 256 * ELEMS): thread i keeps
+// rows [i ELEMS, (i + 1) ELEMS) of W_g (8 bf16 = 16 bytes per row) in
+// registers and walks the tokens blockIdx.x, blockIdx.x + gridDim.x, ...,
+// prefetching the next token's slice of x while it reduces the current one.
+// W_g is then read once per workgroup instead of once per token.  Per token:
+// ELEMS * 8 fp32 FMAs per thread, a wave butterfly and a fixed-order sum of
+// the 4 waves' partials in LDS (deterministic), then thread 0 takes TopK
+// (ties to the lower index) and the softmax.  The pre-normalised variant
+// also sums x^2; every thread forms rstd from the same LDS partials (same
+// order, same value) and writes its slice of u.
+template <int ELEMS, bool NORM>
+__global__ __launch_bounds__(256) void router_resident_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int64_t T, int d, int K,
+    float eps, int32_t* __restrict__ idx, float* __restrict__ gate,
+    uint16_t* __restrict__ u_out) {
+    constexpr int NE = 8;
+    constexpr int XV = ELEMS / 8;  // 16-byte chunks of x per thread
+    __shared__ float part[2][4][NE + 1];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    const int k0 = tid * ELEMS;
+    uint4 w[ELEMS];
+#pragma unroll
+    for (int j = 0; j < ELEMS; ++j) w[j] = *reinterpret_cast<const uint4*>(wg + (int64_t)(k0 + j) * NE);
+    auto wget = [&](int j, int e) {
+        const uint32_t v = e < 2 ? w[j].x : e < 4 ? w[j].y : e < 6 ? w[j].z : w[j].w;
+        return (e & 1) ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
+    };
+    auto load = [&](uint4(&xv)[XV], int64_t t) {
+        const uint4* p = reinterpret_cast<const uint4*>(x + t * (int64_t)d + k0);
+#pragma unroll
+        for (int c = 0; c < XV; ++c) xv[c] = p[c];
+    };
+    auto xget = [&](const uint4(&xv)[XV], int j) {
+        const uint4& c = xv[j / 8];
+        const int e = j % 8;
+        const uint32_t v = e < 2 ? c.x : e < 4 ? c.y : e < 6 ? c.z : c.w;
+        return (e & 1) ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
+    };
+    int64_t t = blockIdx.x;
+    uint4 xv[XV];
+    if (t < T) load(xv, t);
+    for (int par = 0; t < T; t += gridDim.x, par ^= 1) {
+        uint4 xn[XV];
+        const int64_t tn = t + gridDim.x;
+        if (tn < T) load(xn, tn);
+        float acc[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < ELEMS; ++j) {
+            const float xf = xget(xv, j);
+            if (NORM) ss = fmaf(xf, xf, ss);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[e] = fmaf(xf, wget(j, e), acc[e]);
+        }
+        // Reduce-scatter over the wave: the xor-32/16/8 exchanges halve the
+        // values a lane keeps (4 + 2 + 1 shuffles), the xor-4/2/1 butterfly
+        // finishes the sums; lane 8 e' then holds logit e' = lane bits 5..3.
+        float v4[4], v2[2];
+        const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float mine = b5 ? acc[4 + i] : acc[i], other = b5 ? acc[i] : acc[4 + i];
+            v4[i] = mine + __shfl_xor(other, 32, kWave);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float mine = b4 ? v4[2 + i] : v4[i], other = b4 ? v4[i] : v4[2 + i];
+            v2[i] = mine + __shfl_xor(other, 16, kWave);
+        }
+        float v1 = (b3 ? v2[1] : v2[0]) + __shfl_xor(b3 ? v2[0] : v2[1], 8, kWave);
+        v1 += __shfl_xor(v1, 4, kWave);
+        v1 += __shfl_xor(v1, 2, kWave);
+        v1 += __shfl_xor(v1, 1, kWave);
+        if (NORM) ss = wave_sum(ss);
+        if ((lane & 7) == 0) part[par][wv][lane >> 3] = v1;
+        if (NORM && lane == 0) part[par][wv][NE] = ss;
+        __syncthreads();
+        float rstd = 1.0f;
+        if (NORM) {
+            const float sst = (part[par][0][NE] + part[par][1][NE]) +
+                              (part[par][2][NE] + part[par][3][NE]);
+            rstd = 1.0f / sqrtf(sst / (float)d + eps);
+        }
+        if (tid == 0) {
+            float l[NE];
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                l[e] = ((part[par][0][e] + part[par][1][e]) + (part[par][2][e] + part[par][3][e])) *
+                       rstd;
+            uint32_t taken = 0;
+            int sel[8];
+            float val[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < K) {
+                    int best = -1;
+                    float bv = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) {
+                        if (!((taken >> e) & 1u) && (best < 0 || l[e] > bv)) {
+                            best = e;
+                            bv = l[e];
+                        }
+                    }
+                    taken |= 1u << best;
+                    sel[j] = best;
+                    val[j] = bv;
+                }
+            }
+            float g[8];
+            float z = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < K) {
+                    g[j] = expf(val[j] - val[0]);
+                    z += g[j];
+                }
+            }
+            const float rz = 1.0f / z;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < K) {
+                    idx[t * K + j] = sel[j];
+                    gate[t * K + j] = g[j] * rz;
+                }
+            }
+        }
+        if (NORM) {
+            uint4* up = reinterpret_cast<uint4*>(u_out + t * (int64_t)d + k0);
+#pragma unroll
+            for (int c = 0; c < XV; ++c) {
+                uint4 o;
+                o.x = pack_bf16x2(xget(xv, 8 * c + 0) * rstd, xget(xv, 8 * c + 1) * rstd);
+                o.y = pack_bf16x2(xget(xv, 8 * c + 2) * rstd, xget(xv, 8 * c + 3) * rstd);
+                o.z = pack_bf16x2(xget(xv, 8 * c + 4) * rstd, xget(xv, 8 * c + 5) * rstd);
+                o.w = pack_bf16x2(xget(xv, 8 * c + 6) * rstd, xget(xv, 8 * c + 7) * rstd);
+                up[c] = o;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < XV; ++c) xv[c] = xn[c];
+    }
+}
+
+template <bool NORM>
+hipError_t launch_router_resident(const void* x, const void* wg, int64_t T, int d, int K,
+                                  float eps, int32_t* idx, float* gate, void* u_out,
+                                  hipStream_t s) {
+    const dim3 grid((unsigned)(T < 512 ? T : 512));
+    const dim3 block(256);
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const uint16_t* wp = static_cast<const uint16_t*>(wg);
+    uint16_t* up = static_cast<uint16_t*>(u_out);
+    if (d == 2048)
+        hipLaunchKernelGGL((router_resident_kernel<8, NORM>), grid, block, 0, s, xp, wp, T, d, K,
+                           eps, idx, gate, up);
+    else if (d == 4096)
+        hipLaunchKernelGGL((router_resident_kernel<16, NORM>), grid, block, 0, s, xp, wp, T, d,
+                           K, eps, idx, gate, up);
+    else
+        hipLaunchKernelGGL((router_resident_kernel<32, NORM>), grid, block, 0, s, xp, wp, T, d,
+                           K, eps, idx, gate, up);
+    return hipGetLastError();
+}
+
 template <typename TIn, bool NORM>
 hipError_t launch_router_t(const void* x, const void* wg, int64_t T, int d, int n, int K,
                            float eps, int32_t* idx, float* gate, void* u_out,
@@ -217,6 +385,9 @@ hipError_t launch_router_t(const void* x, const void* wg, int64_t T, int d, int 
 hipError_t launch_router(bool bf16, bool norm, const void* x, const void* wg, int64_t T,
                          int d, int n, int K, float eps, int32_t* idx, float* gate,
                          void* u_out, hipStream_t s) {
+    if (bf16 && n == 8 && (d == 2048 || d == 4096 || d == 8192))
+        return norm ? launch_router_resident<true>(x, wg, T, d, K, eps, idx, gate, u_out, s)
+                    : launch_router_resident<false>(x, wg, T, d, K, eps, idx, gate, u_out, s);
     if (bf16)
         return norm ? launch_router_t<uint16_t, true>(x, wg, T, d, n, K, eps, idx, gate,
                                                       u_out, s)
