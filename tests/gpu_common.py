@@ -69,6 +69,7 @@ def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows
     rep = P.routing_report(gi, gg, lg, oi, og, K)
     assert not rep["bad"], f"routing mismatch on tokens {rep['bad'][:10]}"
     assert np.array_equal(gc, np.bincount(gi.ravel(), minlength=n)), "counts_out"
+    rep["counts"] = [int(c) for c in gc]
     rows = np.arange(T) if rows is None else np.asarray(rows)
 
     def ofn(rows, forced):
