@@ -21,13 +21,13 @@
 // AGPRs, one wave per SIMD); per 16-deep K sub-step a wave reads 4 A and 4 B
 // fragments from LDS for 16 MFMAs.  Down: eight waves of 128 x 64 (two per
 // SIMD, so a wave stalled on a load does not idle its SIMD's MFMA unit).  A
-// workgroup owns 256 token rows x 256 B rows (waves 2 x 2 or 2 x 4), or -- for an
-// expert's last gate/up row tile when it has at most 128 rows -- 128 token
-// rows x 512 B rows (waves 1 x 4), the same MFMA work over twice the
-// columns, so a short tail costs half a tile instead of a whole one.  Both operands are
-// K-contiguous ([out][in] weights), the per-lane 8-element K run each MFMA
-// operand wants; the weights are the MFMA's first operand, so a lane ends up
-// owning 4 contiguous output columns.
+// workgroup owns 256 token rows x 256 B rows (waves 2 x 2 or 2 x 4), or --
+// for an expert's last gate/up row tile when it has at most 128 rows -- 128
+// token rows x 512 B rows (waves 1 x 4), the same MFMA work over twice the
+// columns, so a short tail costs half a tile instead of a whole one.  Both
+// operands are K-contiguous ([out][in] weights), the per-lane 8-element K
+// run each MFMA operand wants; the weights are the MFMA's first operand, so
+// a lane ends up owning 4 contiguous output columns.
 //
 // Pipeline.  Two LDS stages of 64-deep A and B tiles (rows of 128 bytes, the
 // 16-byte chunk XOR-swizzled by (row / 2) % 8 so that the fragment reads of
