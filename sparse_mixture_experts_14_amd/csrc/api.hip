@@ -50,8 +50,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 // environment variable MOE_GEMM_PATH=tiled|skinny forces a bf16 path (a
 // testing and tuning knob).
 // Upper bound of the K splits of the down projection (partial sums in the
-// workspace): up to 8 for the skinny kernel (few rows), 2 for the tiled one.
-int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 2; }
+// workspace): up to 8 for the skinny kernel (few rows), 4 for the tiled one.
+int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 4; }
 
 // Compute units of the current device (cached per device id).
 int device_cus() {

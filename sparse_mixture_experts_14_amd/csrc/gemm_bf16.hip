@@ -480,11 +480,25 @@ int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_s
     // Expected tiles: every expert's last row tile is half full on average.
     const int64_t mt = (A_rows + 255) / 256 + n / 2;
     const int64_t tiles = mt * ((N + 255) / 256);
-    const int64_t rem = tiles % cus;
-    // A last round at most half full runs twice as many half-length tiles
-    // instead.
-    if (max_splits >= 2 && rem != 0 && rem * 2 <= cus && Kdim >= 64) return 2;
-    return 1;
+    if (tiles <= 0 || Kdim < 64 * 2) return 1;
+    // Time in units of one full-K tile round: S splits run ceil(S tiles /
+    // cus) rounds of 1/S-length tiles, and each split past the first writes
+    // and the combine reads another A x N fp32 partial.  Calibration
+    // (measured): a 64-deep K step of a tile round takes ~2 us, the partial
+    // traffic moves at ~5 bytes/ps.
+    const double unit_us = (double)((Kdim + 63) / 64) * 2.0;
+    const double partial_us = (double)A_rows * (double)N * 8.0 / 5.0e6;
+    int best = 1;
+    double best_t = 1e300;
+    for (int S = 1; S <= max_splits && S <= 4; ++S) {
+        const int64_t rounds = (tiles * S + cus - 1) / cus;
+        const double t = (double)rounds / S * unit_us + (S - 1) * partial_us;
+        if (t < best_t * 0.99) {  // a split must win by 1%
+            best_t = t;
+            best = S;
+        }
+    }
+    return best;
 }
 
 hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,

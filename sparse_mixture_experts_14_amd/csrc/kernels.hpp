@@ -30,8 +30,8 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
                                   hipStream_t s);
 // K splits worth using for the tiled down projection on `cus` compute units
-// (at most max_splits): 2 when the last round of tiles would be at most half
-// full, else 1.  Depends on sizes only.
+// (at most min(max_splits, 4)): the count that minimises tile rounds per split
+// plus the cost of the extra fp32 partial sums.  Depends on sizes only.
 int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_splits);
 // Whether the tiled kernels can take these sizes (32-bit buffer offsets).
 bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N);

@@ -47,9 +47,9 @@ def test_workspace_bytes_bounds(lib):
     T, d, d_ff, n, K = 4096, 4096, 14336, 8, 2
     ws = lib.moe_workspace_bytes(T, d, d_ff, n, K, B.MOE_BF16)
     A = T * K
-    # at least: H (bf16) + two K-split partials of O (fp32) + u (bf16) + the
+    # at least: H (bf16) + four K-split partials of O (fp32) + u (bf16) + the
     # integer arrays
-    need = A * d_ff * 2 + 2 * A * d * 4 + T * d * 2 + 4 * A * 4
+    need = A * d_ff * 2 + 4 * A * d * 4 + T * d * 2 + 4 * A * 4
     assert need <= ws < 1.05 * need + 4096
     # decode: split-K partials of the down projection
     ws16 = lib.moe_workspace_bytes(16, d, d_ff, n, K, B.MOE_BF16)
