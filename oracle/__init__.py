@@ -72,6 +72,9 @@ def _load():
     lib.oracle_block_forward.restype = ctypes.c_int
     lib.oracle_block_forward.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, D,
                                          P, I64, P, P, P, P, P]
+    lib.oracle_backward.restype = ctypes.c_int
+    lib.oracle_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32,
+                                    P, I64, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -189,3 +192,46 @@ def forward(x, Wg, W1, W3, W2, K: int, rows=None, forced=None):
 def block_forward(x, Wg, W1, W3, W2, K: int, eps: float, rows=None, forced=None):
     """A stack layer y = x + MoE(RMSNorm(x)) on the tokens ``rows``."""
     return _layer("oracle_block_forward", x, Wg, W1, W3, W2, K, rows, forced, eps)
+
+
+def backward(x, Wg, W1, W3, W2, dy, K: int, rows=None, forced=None, weights: bool = True):
+    """Gradients of L = sum_t dy_t . y_t (fp64).  Returns a dict with dx[R][d]
+    (tokens ``rows``, all when None) and -- when ``weights`` and rows is None --
+    dWg[d][n], dW1[n][d_ff][d], dW3[n][d_ff][d], dW2[n][d][d_ff]."""
+    x = _f32(x)
+    Wg = _f32(Wg)
+    W1 = _f32(W1)
+    W3 = _f32(W3)
+    W2 = _f32(W2)
+    dy = _f32(dy)
+    T, d = x.shape
+    n = Wg.shape[1]
+    d_ff = W1.shape[1]
+    assert dy.shape == (T, d)
+    assert Wg.shape == (d, n)
+    assert W1.shape == (n, d_ff, d) and W3.shape == (n, d_ff, d)
+    assert W2.shape == (n, d, d_ff)
+    rows_a = None
+    R = T
+    if rows is not None:
+        rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = rows_a.shape[0]
+        weights = False
+    forced_a = None
+    if forced is not None:
+        forced_a = np.ascontiguousarray(np.asarray(forced, dtype=np.int32))
+        assert forced_a.shape == (R, K)
+    out = {"dx": np.empty((R, d), np.float64)}
+    if weights:
+        out["dWg"] = np.empty((d, n), np.float64)
+        out["dW1"] = np.empty((n, d_ff, d), np.float64)
+        out["dW3"] = np.empty((n, d_ff, d), np.float64)
+        out["dW2"] = np.empty((n, d, d_ff), np.float64)
+    lib = _load()
+    rc = lib.oracle_backward(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dy), T, d,
+                             d_ff, n, K, _ptr(rows_a), R, _ptr(forced_a), _ptr(out["dx"]),
+                             _ptr(out.get("dWg")), _ptr(out.get("dW1")), _ptr(out.get("dW3")),
+                             _ptr(out.get("dW2")))
+    if rc != 0:
+        raise ValueError(f"oracle_backward failed (rc={rc})")
+    return out

@@ -305,3 +305,221 @@ int oracle_block_route(const float* x, const float* Wg, int64_t T, int64_t d,
     }
     return err;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer: the gradients of L = sum_t dy_t . y_t by the chain
+ * rule through the same definitions ([G], [Y], [S]).  For token t with kept
+ * experts s_j, gates g_j and expert e = s_j:
+ *   a = W1_e x, b = W3_e x, h = SiLU(a) (*) b, o = W2_e h
+ *   dg_j = dy . o            do = g_j dy
+ *   dh = W2_e^T do           db = dh (*) SiLU(a)
+ *   da = dh (*) b (*) SiLU'(a),  SiLU'(a) = s + a s (1 - s), s = 1/(1 + e^-a)
+ *   dW2_e += do h^T, dW1_e += da x^T, dW3_e += db x^T
+ *   dx += W1_e^T da + W3_e^T db
+ * The gates are the softmax of the kept logits, so for kept expert s_j
+ *   dl_{s_j} = g_j (dg_j - sum_k g_k dg_k)
+ * and every other logit gets 0 (TopK is constant under small changes away
+ * from ties); then dW_g += x dl^T and dx += W_g dl.
+ * ------------------------------------------------------------------------ */
+
+/* Per-slot intermediates of one token, kept for the weight gradients. */
+typedef struct {
+    double* da;  /* [K][d_ff] */
+    double* db;  /* [K][d_ff] */
+    double* h;   /* [K][d_ff] */
+    double* dO;  /* [K][d]    */
+    double* dl;  /* [n]       */
+    int32_t sel[64];
+} slot_grads;
+
+static void token_backward(const float* x, const float* Wg, const float* W1,
+                           const float* W3, const float* W2, const float* dy,
+                           int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                           const int32_t* forced, double* dx, slot_grads* sg,
+                           double* scratch) {
+    double* l = scratch;          /* n */
+    double* a = l + n;            /* d_ff */
+    double* b = a + d_ff;         /* d_ff */
+    double* o = b + d_ff;         /* d */
+    double* dh = o + d;           /* d_ff */
+    double g[64], dg[64];
+    int32_t* sel = sg->sel;
+    for (int32_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int64_t k = 0; k < d; ++k) s += (double)x[k] * (double)Wg[k * n + i];
+        l[i] = s;
+    }
+    if (forced) {
+        for (int32_t j = 0; j < K; ++j) sel[j] = forced[j];
+    } else {
+        topk_select(l, n, K, sel);
+    }
+    masked_softmax(l, sel, K, g);
+    for (int64_t k = 0; k < d; ++k) dx[k] = 0.0;
+    for (int32_t j = 0; j < K; ++j) {
+        const int64_t e = sel[j];
+        const float* w1 = W1 + e * d_ff * d;
+        const float* w3 = W3 + e * d_ff * d;
+        const float* w2 = W2 + e * d * d_ff;
+        double* h = sg->h + j * d_ff;
+        for (int64_t f = 0; f < d_ff; ++f) {
+            double sa = 0.0, sb = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                sa += (double)w1[f * d + k] * (double)x[k];
+                sb += (double)w3[f * d + k] * (double)x[k];
+            }
+            a[f] = sa;
+            b[f] = sb;
+            h[f] = silu(sa) * sb;
+        }
+        double dgj = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            double s = 0.0;
+            for (int64_t f = 0; f < d_ff; ++f) s += (double)w2[c * d_ff + f] * h[f];
+            o[c] = s;
+            dgj += (double)dy[c] * s;
+        }
+        dg[j] = dgj;
+        double* dO = sg->dO + j * d;
+        for (int64_t c = 0; c < d; ++c) dO[c] = g[j] * (double)dy[c];
+        for (int64_t f = 0; f < d_ff; ++f) dh[f] = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            for (int64_t f = 0; f < d_ff; ++f) dh[f] += (double)w2[c * d_ff + f] * dO[c];
+        double* da = sg->da + j * d_ff;
+        double* db = sg->db + j * d_ff;
+        for (int64_t f = 0; f < d_ff; ++f) {
+            const double s = 1.0 / (1.0 + exp(-a[f]));
+            db[f] = dh[f] * a[f] * s;
+            da[f] = dh[f] * b[f] * (s + a[f] * s * (1.0 - s));
+        }
+        for (int64_t f = 0; f < d_ff; ++f)
+            for (int64_t k = 0; k < d; ++k)
+                dx[k] += (double)w1[f * d + k] * da[f] + (double)w3[f * d + k] * db[f];
+    }
+    double gdg = 0.0;
+    for (int32_t j = 0; j < K; ++j) gdg += g[j] * dg[j];
+    for (int32_t i = 0; i < n; ++i) sg->dl[i] = 0.0;
+    for (int32_t j = 0; j < K; ++j) sg->dl[sel[j]] = g[j] * (dg[j] - gdg);
+    for (int64_t k = 0; k < d; ++k) {
+        double s = 0.0;
+        for (int32_t i = 0; i < n; ++i) s += (double)Wg[k * n + i] * sg->dl[i];
+        dx[k] += s;
+    }
+}
+
+/* Gradients of L = sum_t dy_t . y_t.  dy[T][d] is the output gradient;
+ * forced (nullable, [R][K]) replaces TopK as in oracle_forward.  Outputs
+ * (each nullable): dx[R][d] for the tokens in rows[0..R) (all T when rows is
+ * NULL), and -- only when rows is NULL -- dWg[d][n], dW1[n][d_ff][d],
+ * dW3[n][d_ff][d], dW2[n][d][d_ff], each summed over tokens in token order.
+ * Returns 0, -1 on invalid arguments, -2 on allocation failure. */
+int oracle_backward(const float* x, const float* Wg, const float* W1, const float* W3,
+                    const float* W2, const float* dy, int64_t T, int64_t d, int64_t d_ff,
+                    int32_t n, int32_t K, const int64_t* rows, int64_t R,
+                    const int32_t* forced, double* dx, double* dWg, double* dW1,
+                    double* dW3, double* dW2) {
+    if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n) return -1;
+    const int weights = dWg || dW1 || dW3 || dW2;
+    if (rows && weights) return -1;
+    if (!rows) R = T;
+    const size_t per_slot = (size_t)(3 * d_ff + d);
+    /* per-token intermediates; only kept when weight gradients are wanted */
+    double* keep = 0;
+    int32_t* keep_sel = 0;
+    if (weights) {
+        keep = (double*)malloc(sizeof(double) * ((size_t)R * (K * per_slot + n)));
+        keep_sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)R * K);
+        if (!keep || !keep_sel) {
+            free(keep);
+            free(keep_sel);
+            return -2;
+        }
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)(n + 3 * d_ff + 2 * d));
+        double* tmp = (double*)malloc(sizeof(double) * (K * per_slot + n));
+        double* dxt = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!scratch || !tmp || !dxt) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < R; ++r) {
+                const int64_t t = rows ? rows[r] : r;
+                double* base = weights ? keep + (size_t)r * (K * per_slot + n) : tmp;
+                slot_grads sg;
+                sg.da = base;
+                sg.db = sg.da + (size_t)K * d_ff;
+                sg.h = sg.db + (size_t)K * d_ff;
+                sg.dO = sg.h + (size_t)K * d_ff;
+                sg.dl = sg.dO + (size_t)K * d;
+                token_backward(x + t * d, Wg, W1, W3, W2, dy + t * d, d, d_ff, n, K,
+                               forced ? forced + r * K : 0, dxt, &sg, scratch);
+                if (dx)
+                    for (int64_t k = 0; k < d; ++k) dx[r * d + k] = dxt[k];
+                if (weights)
+                    for (int32_t j = 0; j < K; ++j) keep_sel[r * K + j] = sg.sel[j];
+            }
+        }
+        free(scratch);
+        free(tmp);
+        free(dxt);
+    }
+    if (err || !weights) {
+        free(keep);
+        free(keep_sel);
+        return err;
+    }
+    /* Weight gradients: every output entry sums its tokens in token order. */
+    const size_t stride = K * per_slot + n;
+#define SLOT(t, j, off) (keep + (size_t)(t) * stride + (off))
+    if (dWg) {
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < d; ++k)
+            for (int32_t i = 0; i < n; ++i) {
+                double s = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    s += (double)x[t * d + k] * SLOT(t, 0, K * per_slot)[i];
+                dWg[k * n + i] = s;
+            }
+    }
+    if (dW1 || dW3) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t ef = 0; ef < (int64_t)n * d_ff; ++ef) {
+            const int64_t e = ef / d_ff, f = ef % d_ff;
+            for (int64_t k = 0; k < d; ++k) {
+                double s1 = 0.0, s3 = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int32_t j = 0; j < K; ++j)
+                        if (keep_sel[t * K + j] == e) {
+                            const double xv = (double)x[t * d + k];
+                            s1 += SLOT(t, 0, j * d_ff)[f] * xv;
+                            s3 += SLOT(t, 0, (size_t)K * d_ff + j * d_ff)[f] * xv;
+                        }
+                if (dW1) dW1[(e * d_ff + f) * d + k] = s1;
+                if (dW3) dW3[(e * d_ff + f) * d + k] = s3;
+            }
+        }
+    }
+    if (dW2) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t ec = 0; ec < (int64_t)n * d; ++ec) {
+            const int64_t e = ec / d, c = ec % d;
+            for (int64_t f = 0; f < d_ff; ++f) {
+                double s = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int32_t j = 0; j < K; ++j)
+                        if (keep_sel[t * K + j] == e)
+                            s += SLOT(t, 0, 3 * (size_t)K * d_ff + j * d)[c] *
+                                 SLOT(t, 0, 2 * (size_t)K * d_ff + j * d_ff)[f];
+                dW2[(e * d + c) * d_ff + f] = s;
+            }
+        }
+    }
+#undef SLOT
+    free(keep);
+    free(keep_sel);
+    return 0;
+}

@@ -1,0 +1,136 @@
+"""Pins of the oracle's backward pass (gradients of L = sum_t dy_t . y_t).
+
+Each pin checks the fp64 gradients against something other than the
+backward code itself:
+* central finite differences of the oracle's own forward pass, for every
+  element of every input, on tiny shapes away from routing ties;
+* torch fp64 autograd of the two special cases the method reduces to -- a
+  plain SwiGLU FFN (n = 1) and a dense softmax-gated mixture (K = n);
+* invariants: the router-logit gradient of a token sums to zero (the gates
+  are a softmax), so every row of dW_g sums to zero; reordering tokens
+  reorders dx and leaves the weight gradients unchanged (up to summation
+  order); a zero output gradient gives zero gradients.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def _layer(rng, T, d, d_ff, n, scale_x=1.0):
+    x = (scale_x * rng.standard_normal((T, d))).astype(np.float32)
+    Wg = (rng.standard_normal((d, n)) / np.sqrt(d)).astype(np.float32)
+    W1 = (rng.standard_normal((n, d_ff, d)) / np.sqrt(d)).astype(np.float32)
+    W3 = (rng.standard_normal((n, d_ff, d)) / np.sqrt(d)).astype(np.float32)
+    W2 = (rng.standard_normal((n, d, d_ff)) / np.sqrt(d_ff)).astype(np.float32)
+    return x, Wg, W1, W3, W2
+
+
+def _loss(x, Wg, W1, W3, W2, dy, K):
+    y, idx, _, _ = oracle.forward(x, Wg, W1, W3, W2, K)
+    return float(np.sum(y * dy.astype(np.float64))), idx
+
+
+def test_backward_matches_finite_differences():
+    rng = np.random.default_rng(5)
+    T, d, d_ff, n, K = 3, 5, 6, 4, 2
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    g = oracle.backward(x, Wg, W1, W3, W2, dy, K)
+    _, idx0 = _loss(x, Wg, W1, W3, W2, dy, K)
+    inputs = {"dx": x, "dWg": Wg, "dW1": W1, "dW3": W3, "dW2": W2}
+    h = 2.0 ** -9
+    for name, arr in inputs.items():
+        flat = arr.reshape(-1)
+        num = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = np.float32(keep + h)
+            up = float(flat[i]) - float(keep)
+            lp, ip = _loss(x, Wg, W1, W3, W2, dy, K)
+            flat[i] = np.float32(keep - h)
+            dn = float(keep) - float(flat[i])
+            lm, im = _loss(x, Wg, W1, W3, W2, dy, K)
+            flat[i] = keep
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "routing moved"
+            num[i] = (lp - lm) / (up + dn)
+        ana = g[name].reshape(-1)
+        np.testing.assert_allclose(ana, num, rtol=2e-5, atol=2e-6, err_msg=name)
+
+
+def _t64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+def test_single_expert_backward_is_swiglu_autograd():
+    rng = np.random.default_rng(6)
+    T, d, d_ff = 7, 9, 11
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, 1)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    g = oracle.backward(x, Wg, W1, W3, W2, dy, 1)
+    X = _t64(x).requires_grad_()
+    A1, A3, A2 = (_t64(w[0]).requires_grad_() for w in (W1, W3, W2))
+    Y = (F.silu(X @ A1.T) * (X @ A3.T)) @ A2.T
+    (Y * _t64(dy)).sum().backward()
+    np.testing.assert_allclose(g["dx"], X.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW1"][0], A1.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW3"][0], A3.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW2"][0], A2.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dWg"], 0.0, atol=1e-12)  # one expert: gate is always 1
+
+
+def test_dense_mixture_backward_when_K_equals_n():
+    rng = np.random.default_rng(7)
+    T, d, d_ff, n = 6, 8, 10, 4
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    g = oracle.backward(x, Wg, W1, W3, W2, dy, n)
+    X = _t64(x).requires_grad_()
+    G = _t64(Wg).requires_grad_()
+    A1, A3, A2 = (_t64(w).requires_grad_() for w in (W1, W3, W2))
+    gates = torch.softmax(X @ G, dim=1)                       # [T][n]
+    h = F.silu(torch.einsum("td,efd->tef", X, A1)) * torch.einsum("td,efd->tef", X, A3)
+    o = torch.einsum("tef,ecf->tec", h, A2)                    # [T][n][d]
+    Y = (gates[:, :, None] * o).sum(1)
+    (Y * _t64(dy)).sum().backward()
+    for name, ref in (("dx", X), ("dWg", G), ("dW1", A1), ("dW3", A3), ("dW2", A2)):
+        np.testing.assert_allclose(g[name], ref.grad.numpy(), rtol=1e-9, atol=1e-11,
+                                   err_msg=name)
+
+
+def test_router_gradient_rows_sum_to_zero():
+    rng = np.random.default_rng(8)
+    x, Wg, W1, W3, W2 = _layer(rng, 40, 16, 12, 8)
+    dy = rng.standard_normal((40, 16)).astype(np.float32)
+    g = oracle.backward(x, Wg, W1, W3, W2, dy, 2)
+    np.testing.assert_allclose(g["dWg"].sum(axis=1), 0.0, atol=1e-12)
+    assert np.abs(g["dWg"]).max() > 1e-3
+
+
+def test_backward_token_permutation():
+    rng = np.random.default_rng(9)
+    T = 12
+    x, Wg, W1, W3, W2 = _layer(rng, T, 10, 14, 8)
+    dy = rng.standard_normal((T, 10)).astype(np.float32)
+    p = rng.permutation(T)
+    g = oracle.backward(x, Wg, W1, W3, W2, dy, 2)
+    gp = oracle.backward(x[p], Wg, W1, W3, W2, dy[p], 2)
+    assert np.array_equal(gp["dx"], g["dx"][p])  # per token: bitwise
+    for name in ("dWg", "dW1", "dW3", "dW2"):
+        np.testing.assert_allclose(gp[name], g[name], rtol=1e-12, atol=1e-14, err_msg=name)
+    # rows= gives the same per-token dx
+    rows = np.array([3, 0, 11])
+    gr = oracle.backward(x, Wg, W1, W3, W2, dy, 2, rows=rows)
+    assert np.array_equal(gr["dx"], g["dx"][rows])
+
+
+def test_zero_output_gradient():
+    rng = np.random.default_rng(10)
+    x, Wg, W1, W3, W2 = _layer(rng, 5, 8, 6, 4)
+    g = oracle.backward(x, Wg, W1, W3, W2, np.zeros((5, 8), np.float32), 2)
+    for v in g.values():
+        assert not np.any(v)

@@ -7,6 +7,7 @@ import subprocess
 import pytest
 
 import oracle as oracle_pkg
+from tests import test_oracle_backward as bpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
@@ -42,6 +43,53 @@ PIN_TESTS = [
     lambda o: pins.test_duplicate_router_columns_tie_to_lower_index(o),
     lambda o: pins.test_block_layer_is_residual_over_rmsnorm(o),
 ]
+
+
+# Mistakes in the backward pass, each to be rejected by a backward pin.
+BACKWARD_MUTANTS = {
+    "bwd_silu_derivative": ("da[f] = dh[f] * b[f] * (s + a[f] * s * (1.0 - s));",
+                            "da[f] = dh[f] * b[f] * s;"),
+    "bwd_up_branch": ("db[f] = dh[f] * a[f] * s;", "db[f] = dh[f] * s;"),
+    "bwd_softmax_uncentred": ("sg->dl[sel[j]] = g[j] * (dg[j] - gdg);",
+                              "sg->dl[sel[j]] = g[j] * dg[j];"),
+    "bwd_gate_dropped": ("dO[c] = g[j] * (double)dy[c];", "dO[c] = (double)dy[c];"),
+    "bwd_router_dx_dropped": ("        dx[k] += s;\n    }\n}", "        dx[k] += 0.0 * s;\n    }\n}"),
+    "bwd_w1_w3_swapped": ("if (dW1) dW1[(e * d_ff + f) * d + k] = s1;",
+                          "if (dW1) dW1[(e * d_ff + f) * d + k] = s3;"),
+}
+
+BACKWARD_PINS = [
+    lambda o: bpins.test_backward_matches_finite_differences(),
+    lambda o: bpins.test_single_expert_backward_is_swiglu_autograd(),
+    lambda o: bpins.test_dense_mixture_backward_when_K_equals_n(),
+    lambda o: bpins.test_router_gradient_rows_sum_to_zero(),
+]
+
+
+def _build_mutant(old, new, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o",
+                    str(so_path), str(c_path), "-lm"], check=True)
+    monkeypatch.setattr(oracle_pkg, "_LIB_PATH", str(so_path))
+    monkeypatch.setattr(oracle_pkg, "_lib", None)
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutant_is_caught(name, tmp_path, monkeypatch):
+    _build_mutant(*BACKWARD_MUTANTS[name], tmp_path, monkeypatch)
+    caught = 0
+    for pin in BACKWARD_PINS:
+        try:
+            pin(oracle_pkg)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    monkeypatch.setattr(oracle_pkg, "_lib", None)
+    assert caught > 0, f"no backward pin rejects the mutant {name}"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
