@@ -140,6 +140,38 @@ moe_status_t moe_block_forward(const void* x, const void* w_g, const void* w1,
                                float* gate_out, int32_t* counts_out,
                                void* stream);
 
+/* Bytes of workspace that moe_backward needs for these sizes (an upper bound
+ * that does not depend on the routing).  Returns 0 if the sizes are invalid
+ * or dt is not MOE_BF16. */
+size_t moe_backward_workspace_bytes(int64_t T, int64_t d, int64_t d_ff,
+                                    int32_t n, int32_t K, moe_dtype_t dt);
+
+/* Backward pass of the layer of moe_forward: the gradients of the scalar
+ * L = sum_t dy_t . y_t with respect to every input, differentiating the gate
+ * and output equations of the "Method" section.  TopK is piecewise constant,
+ * so only the K kept logits of a token receive a gradient, through the
+ * softmax over them:
+ *   dg_j = dy . SwiGLU_{s_j}(x),  dl_{s_j} = g_j (dg_j - sum_k g_k dg_k).
+ * The routing is recomputed from (x, W_g) exactly as moe_forward computes it.
+ * Inputs x, W_g, W1, W3, W2 as in moe_forward and dy [T][d] (all MOE_BF16).
+ * Outputs (overwritten, none may overlap an input, another output or the
+ * workspace):
+ *   dx   [T][d]         bf16, fp32 sums rounded once (RNE)
+ *   dw_g [d][n]         float
+ *   dw1, dw3 [n][d_ff][d], dw2 [n][d][d_ff]   float
+ * Arithmetic: fp32 accumulation; the recomputed pre-activations, the hidden
+ * activation, g dy and the SwiGLU input gradients are rounded to bf16 before
+ * the products that consume them.  workspace: at least
+ * moe_backward_workspace_bytes(...) bytes, 256-byte aligned.  dt = MOE_F32
+ * returns MOE_ERR_UNSUPPORTED.  T = 0 zeroes the weight gradients (x, dy and
+ * dx may then be NULL). */
+moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
+                          const void* w3, const void* w2, const void* dy,
+                          int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                          int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
+                          float* dw1, float* dw3, float* dw2, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Timing hook (for profilers and benchmarks, not part of the layer): in later
  * moe_forward / moe_block_forward calls made by this thread, record
  * start_event on the call's stream right before `stage` is launched and

@@ -25,7 +25,7 @@ MOE_BF16 = 1
 
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
-           "moe_last_error")
+           "moe_last_error", "moe_backward", "moe_backward_workspace_bytes")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4}
 
 
@@ -69,6 +69,11 @@ def load(path: str | None = None):
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, F,
                                       V, V, SZ, V, V, V, V]
+    lib.moe_backward_workspace_bytes.restype = SZ
+    lib.moe_backward_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, ctypes.c_int]
+    lib.moe_backward.restype = ctypes.c_int
+    lib.moe_backward.argtypes = [V, V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, V, V,
+                                 V, V, V, V, SZ, V]
     if path is None:
         _lib = lib
     return lib
@@ -210,3 +215,39 @@ def block_forward(x, Wg, W1, W3, W2, K: int, eps: float):
     L = Layer(x.shape[0], d, d_ff, n, K, x.dtype, x.device)
     y = L.block_forward(x, Wg, W1, W3, W2, eps)
     return y, L.idx, L.gate, L.counts
+
+
+def backward_workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int,
+                             dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_backward_workspace_bytes(T, d, d_ff, n, K, code))
+
+
+def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None):
+    """Gradients of sum(dy * y) for bf16 inputs: (dx bf16 [T][d], dW_g, dW1,
+    dW3, dW2 float32 in the layouts of W_g, W1, W3, W2)."""
+    T, d = x.shape
+    n, d_ff, _ = W1.shape
+    if Wg.shape != (d, n) or W1.shape != (n, d_ff, d) or W3.shape != (n, d_ff, d) \
+            or W2.shape != (n, d, d_ff) or dy.shape != (T, d):
+        raise ValueError("tensor shapes do not match the layer sizes")
+    for t in (Wg, W1, W3, W2, dy):
+        if t.dtype != x.dtype:
+            raise ValueError("all inputs must share one dtype")
+    nbytes = backward_workspace_bytes(T, d, d_ff, n, K, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    dev = x.device
+    dx = torch.empty_like(x)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dwg = torch.empty(d, n, **f32)
+    dw1 = torch.empty(n, d_ff, d, **f32)
+    dw3 = torch.empty(n, d_ff, d, **f32)
+    dw2 = torch.empty(n, d, d_ff, **f32)
+    st = load().moe_backward(_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"),
+                             _dev(W2, "W2"), _dev(dy, "dy"), T, d, d_ff, n, K, _dtype_code(x),
+                             _dev(dx, "dx"), dwg.data_ptr(), dw1.data_ptr(), dw3.data_ptr(),
+                             dw2.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                             _stream(dev))
+    _check(st, "moe_backward")
+    return {"dx": dx, "dWg": dwg, "dW1": dw1, "dW3": dw3, "dW2": dw2}

@@ -303,6 +303,196 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     return MOE_OK;
 }
 
+// ---- backward -------------------------------------------------------------------
+// Workspace of moe_backward (bf16): routing, recomputed forward pieces,
+// gradients in assignment (expert) order, transposed weights, and transposed,
+// expert-padded activations for the weight gradients.
+struct BwdLayout {
+    size_t idx, gate, offsets, perm, inv, AB, H, O, dg, DO, W2T, DH, DADB, W13T, dl, part, DOT,
+        HT, DAT, DBT, XT, total;
+    int64_t Kp;  // padded assignment columns of the transposed activations
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
+    const size_t A = (size_t)T * (size_t)K;
+    const size_t dd = (size_t)d, ff = (size_t)d_ff;
+    BwdLayout L{};
+    L.Kp = ((int64_t)A + (int64_t)n * 63 + 63) / 64 * 64;
+    const size_t Kp = (size_t)L.Kp;
+    size_t o = 0;
+    L.idx = o;     o = align256(o + A * 4);
+    L.gate = o;    o = align256(o + A * 4);
+    L.offsets = o; o = align256(o + (size_t)(n + 1) * 4);
+    L.perm = o;    o = align256(o + A * 4);
+    L.inv = o;     o = align256(o + A * 4);
+    L.AB = o;      o = align256(o + A * 2 * ff * 2);
+    L.H = o;       o = align256(o + A * ff * 2);
+    L.O = o;       o = align256(o + A * dd * 4);  // expert outputs, later dx per assignment
+    L.dg = o;      o = align256(o + A * 4);
+    L.DO = o;      o = align256(o + A * dd * 2);
+    L.W2T = o;     o = align256(o + (size_t)n * ff * dd * 2);
+    L.DH = o;      o = align256(o + A * ff * 4);
+    L.DADB = o;    o = align256(o + A * 2 * ff * 2);
+    L.W13T = o;    o = align256(o + (size_t)n * dd * 2 * ff * 2);
+    L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
+    L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
+    L.DOT = o;     o = align256(o + dd * Kp * 2);
+    L.HT = o;      o = align256(o + ff * Kp * 2);
+    L.DAT = o;     o = align256(o + ff * Kp * 2);
+    L.DBT = o;     o = align256(o + ff * Kp * 2);
+    L.XT = o;      o = align256(o + dd * Kp * 2);
+    L.total = o;
+    return L;
+}
+
+moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, const void* w3,
+                            const void* w2, const void* dy, int64_t T, int64_t d, int64_t d_ff,
+                            int32_t n, int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
+                            float* dw1, float* dw3, float* dw2, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    const char* fn = "moe_backward";
+    moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
+    if (st != MOE_OK) return st;
+    if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+    const void* ptrs[] = {x, w_g, w1, w3, w2, dy, dx, dw_g, dw1, dw3, dw2};
+    const char* names[] = {"x", "w_g", "w1", "w3", "w2", "dy", "dx", "dw_g", "dw1", "dw3", "dw2"};
+    for (int i = 0; i < 11; ++i) {
+        const bool rows = i == 0 || i == 5 || i == 6;  // x, dy, dx hold T rows
+        if (!ptrs[i] && T == 0 && rows) continue;
+        if (!ptrs[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
+        if (!aligned(ptrs[i], 16))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
+    }
+    const int64_t A = T * K;
+    if (!moe::tiled_fits(T, d, d_ff) || !moe::tiled_fits(A, d_ff, d) ||
+        !moe::tiled_fits(A, 2 * d_ff, d) || !moe::tiled_fits(A, d, d_ff))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: operands must stay below 2 GiB; split the tokens",
+                    fn);
+    const BwdLayout L = bwd_layout(T, d, d_ff, n, K);
+    if ((int64_t)d_ff * L.Kp * 2 >= (int64_t(1) << 31) || (int64_t)d * L.Kp * 2 >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: too many tokens for the weight gradients", fn);
+    if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
+    if (!aligned(workspace, 256))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
+    if (ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", fn,
+                    ws_bytes, L.total);
+    const size_t xbytes = (size_t)T * (size_t)d * 2;
+    const size_t wbytes = (size_t)n * (size_t)d_ff * (size_t)d;
+    const void* outs[] = {dx, dw_g, dw1, dw3, dw2, workspace};
+    const size_t osz[] = {xbytes, (size_t)d * n * 4, wbytes * 4, wbytes * 4, wbytes * 4, L.total};
+    const void* ins[] = {x, w_g, w1, w3, w2, dy};
+    const size_t isz[] = {xbytes, (size_t)d * n * 2, wbytes * 2, wbytes * 2, wbytes * 2, xbytes};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], osz[i], ins[j], isz[j]))
+                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", fn);
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], osz[i], outs[j], osz[j]))
+                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", fn);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t err = hipSuccess;
+    if (T == 0) {  // no tokens: every weight gradient is zero
+        err = hipMemsetAsync(dw_g, 0, (size_t)d * n * 4, s);
+        if (err == hipSuccess) err = hipMemsetAsync(dw1, 0, wbytes * 4, s);
+        if (err == hipSuccess) err = hipMemsetAsync(dw3, 0, wbytes * 4, s);
+        if (err == hipSuccess) err = hipMemsetAsync(dw2, 0, wbytes * 4, s);
+        if (err != hipSuccess) return hip_fail(err, "zero gradients");
+        g_last_error[0] = '\0';
+        return MOE_OK;
+    }
+    char* ws = static_cast<char*>(workspace);
+    auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+    int32_t* idx = static_cast<int32_t*>(at(L.idx));
+    float* gate = static_cast<float*>(at(L.gate));
+    int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
+    int32_t* perm = static_cast<int32_t*>(at(L.perm));
+    int32_t* inv = static_cast<int32_t*>(at(L.inv));
+    uint16_t* AB = static_cast<uint16_t*>(at(L.AB));
+    uint16_t* H = static_cast<uint16_t*>(at(L.H));
+    float* O = static_cast<float*>(at(L.O));
+    float* DX = O;  // O is consumed (dg) before the dx products are written
+    float* dg = static_cast<float*>(at(L.dg));
+    uint16_t* DO = static_cast<uint16_t*>(at(L.DO));
+    uint16_t* W2T = static_cast<uint16_t*>(at(L.W2T));
+    float* DH = static_cast<float*>(at(L.DH));
+    uint16_t* DADB = static_cast<uint16_t*>(at(L.DADB));
+    uint16_t* W13T = static_cast<uint16_t*>(at(L.W13T));
+    float* dl = static_cast<float*>(at(L.dl));
+    float* part = static_cast<float*>(at(L.part));
+    uint16_t* DOT = static_cast<uint16_t*>(at(L.DOT));
+    uint16_t* HT = static_cast<uint16_t*>(at(L.HT));
+    uint16_t* DAT = static_cast<uint16_t*>(at(L.DAT));
+    uint16_t* DBT = static_cast<uint16_t*>(at(L.DBT));
+    uint16_t* XT = static_cast<uint16_t*>(at(L.XT));
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* w1b = static_cast<const uint16_t*>(w1);
+    const uint16_t* w3b = static_cast<const uint16_t*>(w3);
+    const uint16_t* w2b = static_cast<const uint16_t*>(w2);
+    const int D = (int)d, F = (int)d_ff;
+    const int64_t Kp = L.Kp;
+#define STEP(call, what)                                  \
+    do {                                                  \
+        if (err == hipSuccess) {                          \
+            err = (call);                                 \
+            if (err != hipSuccess) return hip_fail(err, what); \
+        }                                                 \
+    } while (0)
+    // forward pieces: routing, pre-activations, H, expert outputs
+    STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s), "router");
+    STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
+    STEP(moe::launch_gemm_bf16_gateup_ab(xb, T, perm, K, w1b, w3b, offsets, n, A, D, F, AB, s),
+         "gate/up recompute");
+    STEP(moe::launch_bwd_h(AB, A, F, H, s), "h");
+    STEP(moe::launch_gemm_bf16_tiled(false, H, A, nullptr, K, w2b, nullptr, offsets, n, A, F, D,
+                                     O, 1, s),
+         "down recompute");
+    // gate gradients and do = g dy
+    STEP(moe::launch_bwd_gates(static_cast<const uint16_t*>(dy), O, perm, gate, A, K, D, dg, DO,
+                               s),
+         "gate gradients");
+    // dh = do W2 (W2 transposed per expert to [d_ff][d])
+    STEP(moe::launch_transpose(w2b, D, F, F, 0, (int64_t)D * F, W2T, D, 0, (int64_t)F * D, n, s),
+         "W2 transpose");
+    STEP(moe::launch_gemm_bf16_tiled(false, DO, A, nullptr, K, W2T, nullptr, offsets, n, A, D, F,
+                                     DH, 1, s),
+         "dh product");
+    STEP(moe::launch_bwd_swiglu(AB, DH, A, F, DADB, s), "SwiGLU backward");
+    // dx per assignment = [da | db] [W1 ; W3] (weights transposed to [d][2 d_ff])
+    STEP(moe::launch_transpose(w1b, F, D, D, 0, (int64_t)F * D, W13T, 2 * (int64_t)F, 0,
+                               (int64_t)D * 2 * F, n, s),
+         "W1 transpose");
+    STEP(moe::launch_transpose(w3b, F, D, D, 0, (int64_t)F * D, W13T, 2 * (int64_t)F, F,
+                               (int64_t)D * 2 * F, n, s),
+         "W3 transpose");
+    STEP(moe::launch_gemm_bf16_tiled(false, DADB, A, nullptr, K, W13T, nullptr, offsets, n, A,
+                                     2 * F, D, DX, 1, s),
+         "dx product");
+    // router gradient, dx back in token order, dW_g
+    STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, inv, T, K,
+                               n, D, dl, static_cast<uint16_t*>(dx), s),
+         "token gradients");
+    STEP(moe::launch_bwd_dwg(xb, dl, T, D, n, part, dw_g, s), "router weight gradient");
+    // weight gradients of the experts over each expert's assignments
+    STEP(moe::launch_transpose_pad(DO, D, D, 0, offsets, n, nullptr, K, Kp, DOT, s), "do^T");
+    STEP(moe::launch_transpose_pad(H, F, F, 0, offsets, n, nullptr, K, Kp, HT, s), "h^T");
+    STEP(moe::launch_transpose_pad(DADB, F, 2 * (int64_t)F, 0, offsets, n, nullptr, K, Kp, DAT,
+                                   s),
+         "da^T");
+    STEP(moe::launch_transpose_pad(DADB, F, 2 * (int64_t)F, F, offsets, n, nullptr, K, Kp, DBT,
+                                   s),
+         "db^T");
+    STEP(moe::launch_transpose_pad(xb, D, D, 0, offsets, n, perm, K, Kp, XT, s), "x^T");
+    STEP(moe::launch_gemm_bf16_wgrad(DOT, HT, offsets, n, (int)Kp, D, F, dw2, s), "dW2");
+    STEP(moe::launch_gemm_bf16_wgrad(DAT, XT, offsets, n, (int)Kp, F, D, dw1, s), "dW1");
+    STEP(moe::launch_gemm_bf16_wgrad(DBT, XT, offsets, n, (int)Kp, F, D, dw3, s), "dW3");
+#undef STEP
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +581,21 @@ moe_status_t moe_block_forward(const void* x, const void* w_g, const void* w1, c
                                int32_t* counts_out, void* stream) {
     return layer_forward(true, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, eps, y, workspace,
                          workspace_bytes, idx_out, gate_out, counts_out, stream);
+}
+
+size_t moe_backward_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                                    moe_dtype_t dt) {
+    if (check_sizes(T, d, d_ff, n, K, dt, true) != MOE_OK || dt != MOE_BF16) return 0;
+    return bwd_layout(T, d, d_ff, n, K).total;
+}
+
+moe_status_t moe_backward(const void* x, const void* w_g, const void* w1, const void* w3,
+                          const void* w2, const void* dy, int64_t T, int64_t d, int64_t d_ff,
+                          int32_t n, int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
+                          float* dw1, float* dw3, float* dw2, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
+                          workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

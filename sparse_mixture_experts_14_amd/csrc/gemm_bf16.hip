@@ -91,7 +91,10 @@ struct TileArgs {
 // One output tile: loads, MFMA main loop and epilogue.  S0 and S1 are the two
 // LDS stages (separate objects, so the compiler can tell the stage being read
 // from the stage being filled).
-template <bool GATEUP, bool KTAIL, class SH, int STG>
+// EPI (gate/up only): 0 stores H = bf16(SiLU(a) * b); 1 stores the
+// pre-activations themselves, a and b in bf16, as rows [a | b] of 2 N columns
+// (the backward pass needs them).
+template <bool GATEUP, bool KTAIL, class SH, int STG, int EPI = 0>
 __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_t* S1) {
     constexpr int BM = SH::BM, BN = SH::BN, WM = SH::WM, WN = SH::WN, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (accumulator space)
@@ -301,49 +304,62 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     const int col_w = n0 + wn * OCOLS;  // first output column of this wave
     constexpr int CPR = OCOLS * ES / 16;      // 16-byte chunks per staged row
     constexpr int RPI = kWave / CPR;          // rows per store instruction
+    constexpr bool AB = GATEUP && EPI == 1;
+    const int64_t out_stride = AB ? 2 * (int64_t)N : N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        // stage rows wm*WTM + 32i .. +31
 #pragma unroll
-        for (int j = 0; j < (GATEUP ? TN / 2 : TN); ++j) {
+        for (int half = 0; half < (AB ? 2 : 1); ++half) {
+            // stage rows wm*WTM + 32i .. +31
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = j * 32 + 8 * q + 4 * khalf;  // column within the wave
-                uint8_t* dst = slot + l32 * RSTRIDE + c * ES;
-                if (GATEUP) {
-                    const f32x16_t& g = acc[i][j];
-                    const f32x16_t& u = acc[i][j + TN / 2];
-                    u32x2_t h;
-                    h.x = pack_bf16x2(silu_bf16out(g[4 * q + 0]) * u[4 * q + 0],
-                                      silu_bf16out(g[4 * q + 1]) * u[4 * q + 1]);
-                    h.y = pack_bf16x2(silu_bf16out(g[4 * q + 2]) * u[4 * q + 2],
-                                      silu_bf16out(g[4 * q + 3]) * u[4 * q + 3]);
-                    *reinterpret_cast<u32x2_t*>(dst) = h;
-                } else {
-                    const f32x16_t& a = acc[i][j];
-                    *reinterpret_cast<f32x4_t*>(dst) =
-                        f32x4_t{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            for (int j = 0; j < (GATEUP ? TN / 2 : TN); ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = j * 32 + 8 * q + 4 * khalf;  // column within the wave
+                    uint8_t* dst = slot + l32 * RSTRIDE + c * ES;
+                    if (AB) {
+                        const f32x16_t& v = acc[i][j + half * (TN / 2)];
+                        u32x2_t h;
+                        h.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
+                        h.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+                        *reinterpret_cast<u32x2_t*>(dst) = h;
+                    } else if (GATEUP) {
+                        const f32x16_t& g = acc[i][j];
+                        const f32x16_t& u = acc[i][j + TN / 2];
+                        u32x2_t h;
+                        h.x = pack_bf16x2(silu_bf16out(g[4 * q + 0]) * u[4 * q + 0],
+                                          silu_bf16out(g[4 * q + 1]) * u[4 * q + 1]);
+                        h.y = pack_bf16x2(silu_bf16out(g[4 * q + 2]) * u[4 * q + 2],
+                                          silu_bf16out(g[4 * q + 3]) * u[4 * q + 3]);
+                        *reinterpret_cast<u32x2_t*>(dst) = h;
+                    } else {
+                        const f32x16_t& a = acc[i][j];
+                        *reinterpret_cast<f32x4_t*>(dst) =
+                            f32x4_t{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    }
                 }
             }
-        }
-        // write back: lane -> (row, 16-byte chunk).  The slot is the wave's own
-        // and LDS operations of one wave complete in order: no barrier needed.
+            // write back: lane -> (row, 16-byte chunk).  The slot is the wave's
+            // own and LDS operations of one wave complete in order: no barrier
+            // needed (also before the second half overwrites the slot).
 #pragma unroll
-        for (int rr2 = 0; rr2 < 32; rr2 += RPI) {
-            const int r = rr2 + lane / CPR, ch = lane % CPR;
-            const int row = wm * WTM + i * 32 + r;
-            const int col = col_w + ch * (16 / ES);
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + r * RSTRIDE + ch * 16);
-            if (row < rows && col < N) {
-                uint8_t* out = static_cast<uint8_t*>(t.Cout) +
-                               ((int64_t)(t.row0 + row) * N + col) * ES;
-                *reinterpret_cast<u32x4_t*>(out) = v;
+            for (int rr2 = 0; rr2 < 32; rr2 += RPI) {
+                const int r = rr2 + lane / CPR, ch = lane % CPR;
+                const int row = wm * WTM + i * 32 + r;
+                const int col = col_w + ch * (16 / ES);
+                const u32x4_t v =
+                    *reinterpret_cast<const u32x4_t*>(slot + r * RSTRIDE + ch * 16);
+                if (row < rows && col < N) {
+                    uint8_t* out = static_cast<uint8_t*>(t.Cout) +
+                                   ((int64_t)(t.row0 + row) * out_stride + half * N + col) * ES;
+                    *reinterpret_cast<u32x4_t*>(out) = v;
+                }
             }
         }
     }
 }
 
-template <bool GATEUP, bool KTAIL, int NWV>
+template <bool GATEUP, bool KTAIL, int NWV, int EPI>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
@@ -432,16 +448,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         t.row0 = start + mt * SQ::BM;
         t.rows = min(SQ::BM, end - t.row0);
         t.n0 = (2 * c + L / gm) * BNO_S;
-        tile_body<GATEUP, KTAIL, SQ, STG>(t, S0, S1);
+        tile_body<GATEUP, KTAIL, SQ, STG, EPI>(t, S0, S1);
     } else if constexpr (WIDE_MAX > 0) {
         t.row0 = start + nsq * SQ::BM;
         t.rows = end - t.row0;
         t.n0 = 2 * c * BNO_S;
-        tile_body<GATEUP, KTAIL, WD, STG>(t, S0, S1);
+        tile_body<GATEUP, KTAIL, WD, STG, EPI>(t, S0, S1);
     }
 }
 
-template <bool GATEUP, int NWV = 4>
+template <bool GATEUP, int NWV = 4, int EPI = 0>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
@@ -458,14 +474,61 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     const bool ktail = Kdim % BK != 0;
     const int64_t stride = A_rows * (int64_t)N;
     if (ktail)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, NWV>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
                            N, C, GM, splits, stride);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, NWV>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
                            N, C, GM, splits, stride);
     return hipGetLastError();
+}
+
+// Weight gradients of the grouped products.  For every expert e,
+//   C_e[r][c] = sum over the expert's assignments p of A[r][p] B[c][p],
+// where A [N1][Kp] and B [N2][Kp] hold transposed activations whose columns
+// are the assignments in expert order, each expert's run zero-padded to a
+// multiple of 64 columns (padded offsets poff).  A tile of C_e is a K range
+// of the same square tile body (fp32 out); C_e = C + e N1 N2.
+template <int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
+void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                       const int32_t* __restrict__ offsets, int n, int Kp, int N1, int N2,
+                       float* __restrict__ C) {
+    using SQ = Square<NWV>;
+    constexpr int STG = SQ::STAGE_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t S0[STG];
+    __shared__ __attribute__((aligned(1024))) uint8_t S1[STG];
+    const int mtn = (N1 + SQ::BM - 1) / SQ::BM, ntn = (N2 + SQ::BN - 1) / SQ::BN;
+    const int per_e = mtn * ntn;
+    const int tiles = n * per_e;
+    // each XCD takes one contiguous share; inside an expert the row tile
+    // varies fastest, so consecutive tiles share their B tile
+    const int per_xcd = (tiles + 7) / 8;
+    const int jx = (int)(blockIdx.x >> 3);
+    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
+    if (jx >= per_xcd || L0 >= tiles) return;
+    const int e = L0 / per_e, rem = L0 - e * per_e;
+    int pbeg = 0;
+    for (int q = 0; q < e; ++q) pbeg += (offsets[q + 1] - offsets[q] + BK - 1) / BK * BK;
+    const int pend = pbeg + (offsets[e + 1] - offsets[e] + BK - 1) / BK * BK;
+    TileArgs t;
+    t.A = A;
+    t.A_src_rows = N1;
+    t.perm = nullptr;
+    t.K = 1;
+    t.B1 = B;
+    t.B3 = nullptr;
+    t.Kdim = Kp;
+    t.N = N2;
+    t.Cout = C + (int64_t)e * N1 * N2;
+    const int mt = rem % mtn, nt = rem / mtn;
+    t.row0 = mt * SQ::BM;
+    t.rows = min(SQ::BM, N1 - t.row0);
+    t.n0 = nt * SQ::BN;
+    t.k_begin = pbeg / BK;
+    t.k_end = pend / BK;
+    tile_body<false, false, SQ, STG, 0>(t, S0, S1);
 }
 
 }  // namespace
@@ -515,6 +578,32 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
                                      C, GM, 1, s);
     return launch_tiled<false, 8>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
                                   C, GM, splits, s);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, const int32_t* perm,
+                                      int K, const uint16_t* B1, const uint16_t* B3,
+                                      const int32_t* offsets, int n, int64_t A_rows, int Kdim,
+                                      int N, uint16_t* AB, hipStream_t s) {
+    if (!tiled_fits(A_src_rows, Kdim, N)) return hipErrorInvalidValue;
+    return launch_tiled<true, 4, 1>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
+                                    AB, 8, 1, s);
+}
+
+hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* offsets,
+                                  int n, int Kp, int N1, int N2, float* C, hipStream_t s) {
+    if (Kp % BK != 0 || (int64_t)N1 * Kp * 2 >= (int64_t(1) << 31) ||
+        (int64_t)N2 * Kp * 2 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    const int64_t tiles = (int64_t)n * ((N1 + 255) / 256) * ((N2 + 255) / 256);
+    const int64_t blocks = (tiles + 7) / 8 * 8;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_wgrad_kernel<8>), dim3((unsigned)blocks), dim3(512), 0, s, A, B,
+                       offsets, n, Kp, N1, N2, C);
+    return hipGetLastError();
 }
 
 }  // namespace moe
