@@ -214,6 +214,124 @@ def write_traffic(workload: str, dirs, command: str):
     print(json.dumps({workload: entry}), flush=True)
 
 
+def backward_cpu_baseline(w, L, dy, budget_s: float):
+    """The fp64 oracle's backward, as it stands, on the first tokens of the
+    workload (x and dy rows; all weight gradients of that sub-batch), repeated
+    until ~budget_s."""
+    import oracle
+    H = {k: oracle._f32(v) for k, v in L.items()}
+    dyh = oracle._f32(dy)
+
+    def run(m):
+        oracle.backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K)
+
+    t0 = time.perf_counter()
+    run(1)
+    per_tok = time.perf_counter() - t0
+    m = int(min(w.T, max(1, budget_s / max(per_tok, 1e-9) / 2)))
+    reps, tokens, elapsed = 0, 0, 0.0
+    while elapsed < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        run(m)
+        elapsed += time.perf_counter() - t0
+        tokens += m
+        reps += 1
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"backward of the workload's first {m} tokens (x, dy rows; every "
+                      f"gradient) x{reps}",
+            "seconds": round(elapsed, 2), "cpu": platform.processor() or platform.machine()}
+
+
+def bench_backward(args, w, dev):
+    """One step = one moe_backward call: routing and the forward pieces
+    recomputed, dx and every weight gradient.  The dominant kernel is the
+    weight-gradient product (three launches per step, timed together)."""
+    import torch
+
+    import sparse_mixture_experts_14_amd as moe
+    from sparse_mixture_experts_14_amd import workloads as W
+    if w.name == "stack" or w.dtype != "bf16":
+        raise SystemExit("--backward runs the single-layer bf16 workloads")
+    log(f"[bench] backward workload={w.name} T={w.T} building inputs on {dev}")
+    L = W.make_layer(w, device=dev)
+    g = torch.Generator(device=dev).manual_seed(w.seed + 7)
+    dy = torch.randn(w.T, w.d, generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(moe.backward_workspace_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    grads = moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws)
+
+    def step(ev=None):
+        if ev is not None:
+            moe._lib.set_stage_events_raw("bwd_wgrad", ev[0].handle.value, ev[1].handle.value)
+        else:
+            moe._lib.set_stage_events_raw("bwd_wgrad")
+        moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
+                     out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    every = max(1, args.stage_every)
+    kev = {s: (HipEvent(), HipEvent()) for s in range(args.steps) if s % every == 0}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(kev.get(s))
+    end.record()
+    torch.cuda.synchronize()
+    moe._lib.set_stage_events_raw("bwd_wgrad")
+    ms = start.elapsed_time(end) / args.steps
+    k_ms = [a.elapsed_ms(b) / 3.0 for (a, b) in kev.values()]  # three launches per stage
+    k_avg = sum(k_ms) / len(k_ms)
+    idx, _ = moe.route(L["x"], L["Wg"], w.K)
+    counts = torch.bincount(idx.view(-1).long(), minlength=w.n).cpu().tolist()
+    log(f"[bench] {ms:.4f} ms/step, weight-gradient product {k_avg:.4f} ms per launch")
+    A = w.T * w.K
+    # per launch: one expert weight gradient [n][N1][N2] fp32 written (every
+    # expert, zero or not), the two transposed activation operands read
+    wbytes = w.n * w.d * w.d_ff * 4 + A * (w.d + w.d_ff) * 2
+    flops = 2.0 * A * w.d * w.d_ff
+    if wbytes / (HBM_PEAK_GBS * 1e9) > flops / (BF16_PEAK_TFLOPS * 1e12):
+        ach = wbytes / (k_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops / (k_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    sha = kernel_source_sha(["gemm_bf16.hip", "common.hpp"])
+    roof["traffic"] = traffic_for(w.name + "-backward", sha)
+    roof["kernel"] = "weight-gradient product (MFMA tiles over 64-padded expert runs)"
+    roof["kernel_ms"] = round(k_avg, 5)
+    roof["kernel_samples"] = len(k_ms)
+    roof["algorithmic_bytes"] = wbytes
+    roof["algorithmic_flops"] = flops
+    roof["source_sha"] = sha
+    out = {
+        "metric": "MoE-layer backward tokens/s (all gradients of sum(dy*y); top-2 of 8 "
+                  "SwiGLU, d=4096) + % roofline",
+        "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) tokens and output gradients, N(0,1/fan_in) "
+                "weights)",
+        "config": {"workload": w.name + "-backward", "T": w.T, "d": w.d, "d_ff": w.d_ff,
+                   "n": w.n, "K": w.K, "dtype": w.dtype},
+        "roofline": roof,
+        # forward recompute 6, dh 2, dx 4, weight gradients 6 (x A d d_ff)
+        "step_tflops": round(18.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12, 1),
+        "counts": counts,
+    }
+    if args.cpu_budget > 0:
+        log("[bench] timing the fp64 oracle's backward on the host")
+        out["cpu_baseline"] = backward_cpu_baseline(w, L, dy, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +351,9 @@ def main():
                          "for --workload and exit")
     ap.add_argument("--traffic-command", default="",
                     help="command line recorded with --traffic-from")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward (all gradients of sum(dy * y)) instead of the "
+                         "forward layer")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(args.workload, args.traffic_from, args.traffic_command)
@@ -254,6 +375,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.load()
+    if args.backward:
+        bench_backward(args, w, dev)
+        return
     log(f"[bench] workload={w.name} T={w.T} building inputs on {dev}")
     if w.name == "stack":
         layers = [W.make_stack_layer(w, l, device=dev) for l in range(w.layers)]

@@ -75,13 +75,20 @@ typedef enum moe_dtype {
     MOE_BF16 = 1  /* bf16 storage, fp32 accumulation */
 } moe_dtype_t;
 
-/* Stages of moe_forward / moe_block_forward, in launch order. */
+/* Stages of moe_forward / moe_block_forward and of moe_backward, in launch
+ * order. */
 typedef enum moe_stage {
     MOE_STAGE_ROUTER = 0,   /* logits, TopK, softmax (and RMSNorm in the block layer) */
     MOE_STAGE_PERMUTE = 1,  /* per-expert grouping of the assignments */
     MOE_STAGE_GATE_UP = 2,  /* H = SiLU(u W1^T) * (u W3^T), grouped by expert */
     MOE_STAGE_DOWN = 3,     /* O = H W2^T, grouped by expert */
-    MOE_STAGE_COMBINE = 4   /* y = sum_k gate * O (+ x), back in token order */
+    MOE_STAGE_COMBINE = 4,  /* y = sum_k gate * O (+ x), back in token order */
+    /* stages of moe_backward */
+    MOE_STAGE_BWD_RECOMPUTE = 5, /* routing, [a | b] = u [W1 ; W3]^T, h, expert outputs */
+    MOE_STAGE_BWD_DH = 6,   /* dg, g dy, W2 transposed, dh = (g dy) W2, SwiGLU backward */
+    MOE_STAGE_BWD_DX = 7,   /* W1 / W3 transposed, dx, router gradient, dW_g, and the
+                               transposed activations of the weight gradients */
+    MOE_STAGE_BWD_WGRAD = 8 /* the three weight-gradient products dW2, dW1, dW3 */
 } moe_stage_t;
 
 /* Version of this ABI (MOE_ABI_VERSION of the library that was built). */
@@ -173,7 +180,7 @@ moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
                           size_t workspace_bytes, void* stream);
 
 /* Timing hook (for profilers and benchmarks, not part of the layer): in later
- * moe_forward / moe_block_forward calls made by this thread, record
+ * moe_forward / moe_block_forward / moe_backward calls made by this thread, record
  * start_event on the call's stream right before `stage` is launched and
  * end_event right after it.  Both are caller-owned hipEvent_t handles that
  * must stay valid while set; NULL, NULL clears the hook.  Returns

@@ -26,7 +26,8 @@ MOE_BF16 = 1
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
            "moe_last_error", "moe_backward", "moe_backward_workspace_bytes")
-STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4}
+STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
+          "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
 
 class MoeError(RuntimeError):
@@ -223,9 +224,12 @@ def backward_workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int,
     return int(load().moe_backward_workspace_bytes(T, d, d_ff, n, K, code))
 
 
-def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None):
-    """Gradients of sum(dy * y) for bf16 inputs: (dx bf16 [T][d], dW_g, dW1,
-    dW3, dW2 float32 in the layouts of W_g, W1, W3, W2)."""
+def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None,
+             out: dict | None = None):
+    """Gradients of sum(dy * y) for bf16 inputs: a dict of dx (bf16 [T][d]) and
+    dWg, dW1, dW3, dW2 (float32, in the layouts of W_g, W1, W3, W2).  ``out``
+    (such a dict from an earlier call of the same sizes) is overwritten and
+    returned instead of new tensors."""
     T, d = x.shape
     n, d_ff, _ = W1.shape
     if Wg.shape != (d, n) or W1.shape != (n, d_ff, d) or W3.shape != (n, d_ff, d) \
@@ -237,17 +241,25 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = Non
     nbytes = backward_workspace_bytes(T, d, d_ff, n, K, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    if workspace.numel() < nbytes:
+        raise ValueError("workspace too small")
     dev = x.device
-    dx = torch.empty_like(x)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dwg = torch.empty(d, n, **f32)
-    dw1 = torch.empty(n, d_ff, d, **f32)
-    dw3 = torch.empty(n, d_ff, d, **f32)
-    dw2 = torch.empty(n, d, d_ff, **f32)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = {"dx": torch.empty_like(x), "dWg": torch.empty(d, n, **f32),
+               "dW1": torch.empty(n, d_ff, d, **f32), "dW3": torch.empty(n, d_ff, d, **f32),
+               "dW2": torch.empty(n, d, d_ff, **f32)}
+    shapes = {"dx": (x.dtype, (T, d)), "dWg": (torch.float32, (d, n)),
+              "dW1": (torch.float32, (n, d_ff, d)), "dW3": (torch.float32, (n, d_ff, d)),
+              "dW2": (torch.float32, (n, d, d_ff))}
+    for k, (dt, shp) in shapes.items():
+        if out[k].dtype != dt or tuple(out[k].shape) != shp:
+            raise ValueError(f"out[{k!r}] must be {dt} of shape {shp}")
+    dx, dwg, dw1, dw3, dw2 = (out[k] for k in ("dx", "dWg", "dW1", "dW3", "dW2"))
     st = load().moe_backward(_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"),
                              _dev(W2, "W2"), _dev(dy, "dy"), T, d, d_ff, n, K, _dtype_code(x),
-                             _dev(dx, "dx"), dwg.data_ptr(), dw1.data_ptr(), dw3.data_ptr(),
-                             dw2.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                             _stream(dev))
+                             _dev(dx, "dx"), _dev(dwg, "dW_g"), _dev(dw1, "dW1"),
+                             _dev(dw3, "dW3"), _dev(dw2, "dW2"), workspace.data_ptr(),
+                             workspace.numel(), _stream(dev))
     _check(st, "moe_backward")
-    return {"dx": dx, "dWg": dwg, "dW1": dw1, "dW3": dw3, "dW2": dw2}
+    return out

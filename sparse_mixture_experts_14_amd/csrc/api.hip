@@ -21,7 +21,7 @@ thread_local char g_last_error[512] = "";
 
 // Per-thread timing hooks (moe_set_stage_events): events recorded on the
 // call's stream right before and right after one stage's kernel launch.
-constexpr int kStages = 5;
+constexpr int kStages = 9;
 thread_local hipEvent_t g_ev_start[kStages] = {};
 thread_local hipEvent_t g_ev_end[kStages] = {};
 
@@ -440,7 +440,13 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
             if (err != hipSuccess) return hip_fail(err, what); \
         }                                                 \
     } while (0)
+    auto mark = [&](hipEvent_t ev) {
+        if (ev && err == hipSuccess) err = hipEventRecord(ev, s);
+        if (err != hipSuccess) return false;
+        return true;
+    };
     // forward pieces: routing, pre-activations, H, expert outputs
+    if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s), "router");
     STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
     STEP(moe::launch_gemm_bf16_gateup_ab(xb, T, perm, K, w1b, w3b, offsets, n, A, D, F, AB, s),
@@ -449,6 +455,8 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     STEP(moe::launch_gemm_bf16_tiled(false, H, A, nullptr, K, w2b, nullptr, offsets, n, A, F, D,
                                      O, 1, s),
          "down recompute");
+    if (!mark(g_ev_end[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
+    if (!mark(g_ev_start[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
     // gate gradients and do = g dy
     STEP(moe::launch_bwd_gates(static_cast<const uint16_t*>(dy), O, perm, gate, A, K, D, dg, DO,
                                s),
@@ -460,6 +468,8 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
                                      DH, 1, s),
          "dh product");
     STEP(moe::launch_bwd_swiglu(AB, DH, A, F, DADB, s), "SwiGLU backward");
+    if (!mark(g_ev_end[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
+    if (!mark(g_ev_start[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
     // dx per assignment = [da | db] [W1 ; W3] (weights transposed to [d][2 d_ff])
     STEP(moe::launch_transpose(w1b, F, D, D, 0, (int64_t)F * D, W13T, 2 * (int64_t)F, 0,
                                (int64_t)D * 2 * F, n, s),
@@ -485,9 +495,12 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
                                    s),
          "db^T");
     STEP(moe::launch_transpose_pad(xb, D, D, 0, offsets, n, perm, K, Kp, XT, s), "x^T");
+    if (!mark(g_ev_end[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
+    if (!mark(g_ev_start[MOE_STAGE_BWD_WGRAD])) return hip_fail(err, "event record");
     STEP(moe::launch_gemm_bf16_wgrad(DOT, HT, offsets, n, (int)Kp, D, F, dw2, s), "dW2");
     STEP(moe::launch_gemm_bf16_wgrad(DAT, XT, offsets, n, (int)Kp, F, D, dw1, s), "dW1");
     STEP(moe::launch_gemm_bf16_wgrad(DBT, XT, offsets, n, (int)Kp, F, D, dw3, s), "dW3");
+    if (!mark(g_ev_end[MOE_STAGE_BWD_WGRAD])) return hip_fail(err, "event record");
 #undef STEP
     g_last_error[0] = '\0';
     return MOE_OK;
