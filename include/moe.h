@@ -85,9 +85,8 @@ typedef enum moe_stage {
     MOE_STAGE_COMBINE = 4,  /* y = sum_k gate * O (+ x), back in token order */
     /* stages of moe_backward */
     MOE_STAGE_BWD_RECOMPUTE = 5, /* routing, [a | b] = u [W1 ; W3]^T, h, expert outputs */
-    MOE_STAGE_BWD_DH = 6,   /* dg, g dy, W2 transposed, dh = (g dy) W2, SwiGLU backward */
-    MOE_STAGE_BWD_DX = 7,   /* W1 / W3 transposed, dx, router gradient, dW_g, and the
-                               transposed activations of the weight gradients */
+    MOE_STAGE_BWD_DH = 6,   /* dg, g dy, dh = (g dy) W2, SwiGLU backward */
+    MOE_STAGE_BWD_DX = 7,   /* dx, router gradient, dW_g, tokens gathered per expert */
     MOE_STAGE_BWD_WGRAD = 8 /* the three weight-gradient products dW2, dW1, dW3 */
 } moe_stage_t;
 

@@ -308,17 +308,15 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
 // gradients in assignment (expert) order, transposed weights, and transposed,
 // expert-padded activations for the weight gradients.
 struct BwdLayout {
-    size_t idx, gate, offsets, perm, inv, AB, H, O, dg, DO, W2T, DH, DADB, W13T, dl, part, DOT,
-        HT, DAT, DBT, XT, total;
-    int64_t Kp;  // padded assignment columns of the transposed activations
+    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, total;
 };
+
+constexpr int kBwdMaxSplits = 4;  // K splits of the dx product
 
 BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     const size_t A = (size_t)T * (size_t)K;
     const size_t dd = (size_t)d, ff = (size_t)d_ff;
     BwdLayout L{};
-    L.Kp = ((int64_t)A + (int64_t)n * 63 + 63) / 64 * 64;
-    const size_t Kp = (size_t)L.Kp;
     size_t o = 0;
     L.idx = o;     o = align256(o + A * 4);
     L.gate = o;    o = align256(o + A * 4);
@@ -326,21 +324,15 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.perm = o;    o = align256(o + A * 4);
     L.inv = o;     o = align256(o + A * 4);
     L.AB = o;      o = align256(o + A * 2 * ff * 2);
-    L.H = o;       o = align256(o + A * ff * 2);
-    L.O = o;       o = align256(o + A * dd * 4);  // expert outputs, later dx per assignment
+    L.DX = o;      o = align256(o + kBwdMaxSplits * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
-    L.DO = o;      o = align256(o + A * dd * 2);
-    L.W2T = o;     o = align256(o + (size_t)n * ff * dd * 2);
+    L.DYG = o;     o = align256(o + A * dd * 2);
     L.DH = o;      o = align256(o + A * ff * 4);
     L.DADB = o;    o = align256(o + A * 2 * ff * 2);
-    L.W13T = o;    o = align256(o + (size_t)n * dd * 2 * ff * 2);
+    L.GH = o;      o = align256(o + A * ff * 2);
+    L.XG = o;      o = align256(o + A * dd * 2);
     L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
     L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
-    L.DOT = o;     o = align256(o + dd * Kp * 2);
-    L.HT = o;      o = align256(o + ff * Kp * 2);
-    L.DAT = o;     o = align256(o + ff * Kp * 2);
-    L.DBT = o;     o = align256(o + ff * Kp * 2);
-    L.XT = o;      o = align256(o + dd * Kp * 2);
     L.total = o;
     return L;
 }
@@ -369,8 +361,6 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         return fail(MOE_ERR_UNSUPPORTED, "%s: operands must stay below 2 GiB; split the tokens",
                     fn);
     const BwdLayout L = bwd_layout(T, d, d_ff, n, K);
-    if ((int64_t)d_ff * L.Kp * 2 >= (int64_t(1) << 31) || (int64_t)d * L.Kp * 2 >= (int64_t(1) << 31))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: too many tokens for the weight gradients", fn);
     if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
     if (!aligned(workspace, 256))
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
@@ -411,28 +401,20 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     int32_t* perm = static_cast<int32_t*>(at(L.perm));
     int32_t* inv = static_cast<int32_t*>(at(L.inv));
     uint16_t* AB = static_cast<uint16_t*>(at(L.AB));
-    uint16_t* H = static_cast<uint16_t*>(at(L.H));
-    float* O = static_cast<float*>(at(L.O));
-    float* DX = O;  // O is consumed (dg) before the dx products are written
+    float* DX = static_cast<float*>(at(L.DX));
     float* dg = static_cast<float*>(at(L.dg));
-    uint16_t* DO = static_cast<uint16_t*>(at(L.DO));
-    uint16_t* W2T = static_cast<uint16_t*>(at(L.W2T));
+    uint16_t* DYG = static_cast<uint16_t*>(at(L.DYG));
     float* DH = static_cast<float*>(at(L.DH));
     uint16_t* DADB = static_cast<uint16_t*>(at(L.DADB));
-    uint16_t* W13T = static_cast<uint16_t*>(at(L.W13T));
+    uint16_t* GH = static_cast<uint16_t*>(at(L.GH));
+    uint16_t* XG = static_cast<uint16_t*>(at(L.XG));
     float* dl = static_cast<float*>(at(L.dl));
     float* part = static_cast<float*>(at(L.part));
-    uint16_t* DOT = static_cast<uint16_t*>(at(L.DOT));
-    uint16_t* HT = static_cast<uint16_t*>(at(L.HT));
-    uint16_t* DAT = static_cast<uint16_t*>(at(L.DAT));
-    uint16_t* DBT = static_cast<uint16_t*>(at(L.DBT));
-    uint16_t* XT = static_cast<uint16_t*>(at(L.XT));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* w1b = static_cast<const uint16_t*>(w1);
     const uint16_t* w3b = static_cast<const uint16_t*>(w3);
     const uint16_t* w2b = static_cast<const uint16_t*>(w2);
     const int D = (int)d, F = (int)d_ff;
-    const int64_t Kp = L.Kp;
 #define STEP(call, what)                                  \
     do {                                                  \
         if (err == hipSuccess) {                          \
@@ -445,61 +427,46 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         if (err != hipSuccess) return false;
         return true;
     };
-    // forward pieces: routing, pre-activations, H, expert outputs
+    const int cus = device_cus();
+    const int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
+    // routing and the pre-activations [a | b] recomputed
     if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s), "router");
     STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
     STEP(moe::launch_gemm_bf16_gateup_ab(xb, T, perm, K, w1b, w3b, offsets, n, A, D, F, AB, s),
          "gate/up recompute");
-    STEP(moe::launch_bwd_h(AB, A, F, H, s), "h");
-    STEP(moe::launch_gemm_bf16_tiled(false, H, A, nullptr, K, w2b, nullptr, offsets, n, A, F, D,
-                                     O, 1, s),
-         "down recompute");
     if (!mark(g_ev_end[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
-    // gate gradients and do = g dy
-    STEP(moe::launch_bwd_gates(static_cast<const uint16_t*>(dy), O, perm, gate, A, K, D, dg, DO,
-                               s),
-         "gate gradients");
-    // dh = do W2 (W2 transposed per expert to [d_ff][d])
-    STEP(moe::launch_transpose(w2b, D, F, F, 0, (int64_t)D * F, W2T, D, 0, (int64_t)F * D, n, s),
-         "W2 transpose");
-    STEP(moe::launch_gemm_bf16_tiled(false, DO, A, nullptr, K, W2T, nullptr, offsets, n, A, D, F,
-                                     DH, 1, s),
+    // tokens and output gradients of every assignment in expert order
+    STEP(moe::launch_gather_rows(xb, static_cast<const uint16_t*>(dy), perm, K, A, D, XG, DYG, s),
+         "row gather");
+    // r = dy W2_e (W2_e [d][d_ff] read as K rows), then per row: dg = h . r,
+    // [da | db] of g r, g h
+    STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, 1, s),
          "dh product");
-    STEP(moe::launch_bwd_swiglu(AB, DH, A, F, DADB, s), "SwiGLU backward");
+    STEP(moe::launch_bwd_swiglu(AB, DH, perm, gate, A, F, dg, DADB, GH, s), "SwiGLU backward");
     if (!mark(g_ev_end[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
-    // dx per assignment = [da | db] [W1 ; W3] (weights transposed to [d][2 d_ff])
-    STEP(moe::launch_transpose(w1b, F, D, D, 0, (int64_t)F * D, W13T, 2 * (int64_t)F, 0,
-                               (int64_t)D * 2 * F, n, s),
-         "W1 transpose");
-    STEP(moe::launch_transpose(w3b, F, D, D, 0, (int64_t)F * D, W13T, 2 * (int64_t)F, F,
-                               (int64_t)D * 2 * F, n, s),
-         "W3 transpose");
-    STEP(moe::launch_gemm_bf16_tiled(false, DADB, A, nullptr, K, W13T, nullptr, offsets, n, A,
-                                     2 * F, D, DX, 1, s),
+    // dx per assignment = da W1_e + db W3_e: K rows 0..d_ff-1 from W1_e, the
+    // next d_ff from W3_e, against the rows [da | db]; K-split partials
+    STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, dx_splits,
+                                    s),
          "dx product");
     // router gradient, dx back in token order, dW_g
-    STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, inv, T, K,
-                               n, D, dl, static_cast<uint16_t*>(dx), s),
+    STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, dx_splits,
+                               A, inv, T, K, n, D, dl, static_cast<uint16_t*>(dx), s),
          "token gradients");
     STEP(moe::launch_bwd_dwg(xb, dl, T, D, n, part, dw_g, s), "router weight gradient");
-    // weight gradients of the experts over each expert's assignments
-    STEP(moe::launch_transpose_pad(DO, D, D, 0, offsets, n, nullptr, K, Kp, DOT, s), "do^T");
-    STEP(moe::launch_transpose_pad(H, F, F, 0, offsets, n, nullptr, K, Kp, HT, s), "h^T");
-    STEP(moe::launch_transpose_pad(DADB, F, 2 * (int64_t)F, 0, offsets, n, nullptr, K, Kp, DAT,
-                                   s),
-         "da^T");
-    STEP(moe::launch_transpose_pad(DADB, F, 2 * (int64_t)F, F, offsets, n, nullptr, K, Kp, DBT,
-                                   s),
-         "db^T");
-    STEP(moe::launch_transpose_pad(xb, D, D, 0, offsets, n, perm, K, Kp, XT, s), "x^T");
     if (!mark(g_ev_end[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_WGRAD])) return hip_fail(err, "event record");
-    STEP(moe::launch_gemm_bf16_wgrad(DOT, HT, offsets, n, (int)Kp, D, F, dw2, s), "dW2");
-    STEP(moe::launch_gemm_bf16_wgrad(DAT, XT, offsets, n, (int)Kp, F, D, dw1, s), "dW1");
-    STEP(moe::launch_gemm_bf16_wgrad(DBT, XT, offsets, n, (int)Kp, F, D, dw3, s), "dW3");
+    // weight gradients over each expert's rows: dW2_e = dy^T (g h),
+    // dW1_e = da^T u, dW3_e = db^T u
+    STEP(moe::launch_gemm_bf16_wgrad(DYG, D, GH, F, offsets, n, A, D, F, dw2, s), "dW2");
+    STEP(moe::launch_gemm_bf16_wgrad(DADB, 2 * (int64_t)F, XG, D, offsets, n, A, F, D, dw1, s),
+         "dW1");
+    STEP(moe::launch_gemm_bf16_wgrad(DADB + F, 2 * (int64_t)F, XG, D, offsets, n, A, F, D, dw3,
+                                     s),
+         "dW3");
     if (!mark(g_ev_end[MOE_STAGE_BWD_WGRAD])) return hip_fail(err, "event record");
 #undef STEP
     g_last_error[0] = '\0';

@@ -86,7 +86,26 @@ struct TileArgs {
     void* Cout;           // already offset to this split's partial sums
     int row0, rows, n0;   // tile rows [row0, row0 + rows), first output column
     int k_begin, k_end;   // K steps of this split
+    // K-row operands (stored [K][columns], the tile's M or N columns
+    // contiguous): row stride in elements, the K row of step 0, the first K
+    // row that loads zeros, and the K row where B continues in B3 (row -
+    // b_split) instead of B1.
+    int64_t a_stride = 0, b_stride = 0;
+    int krow0 = 0, klim = 0, b_split = 0;
 };
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes,
+// source lane 4 r + q points at 4 consecutive bf16 of row r; result lane j
+// receives element j of the 16 elements of rows r = 0..3 (r-th value from
+// row r).  With rows = 4 consecutive K and the 4 lanes of a row covering 16
+// consecutive columns, lane j gets 4 consecutive K of column j: the MFMA
+// operand layout, read from a [K][columns] tile.
+__device__ __forceinline__ v4i16_t lds_read_tr(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)(p));
+}
 
 // One output tile: loads, MFMA main loop and epilogue.  S0 and S1 are the two
 // LDS stages (separate objects, so the compiler can tell the stage being read
@@ -94,7 +113,11 @@ struct TileArgs {
 // EPI (gate/up only): 0 stores H = bf16(SiLU(a) * b); 1 stores the
 // pre-activations themselves, a and b in bf16, as rows [a | b] of 2 N columns
 // (the backward pass needs them).
-template <bool GATEUP, bool KTAIL, class SH, int STG, int EPI = 0>
+// AKR / BKR: the A / B operand is a K-row operand ([K][M] / [K][N], rows of
+// K; see TileArgs), staged as [64][BM] / [64][BN] tiles and read with the
+// transposing LDS read; otherwise it is K-contiguous as described above.
+template <bool GATEUP, bool KTAIL, class SH, int STG, int EPI = 0, bool AKR = false,
+          bool BKR = false>
 __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_t* S1) {
     constexpr int BM = SH::BM, BN = SH::BN, WM = SH::WM, WN = SH::WN, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (accumulator space)
@@ -103,6 +126,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     constexpr int STAGE_BYTES = SH::STAGE_BYTES;
     static_assert(TM == 4 && (TN == 4 || TN == 2), "waves of 128 x 128 or 128 x 64");
     static_assert(STAGE_BYTES <= STG, "stage fits (STG: bytes of each stage object)");
+    static_assert(!(GATEUP && (AKR || BKR)), "K-row operands only in plain products");
 
     const int Kdim = t.Kdim, N = t.N, rows = t.rows, n0 = t.n0;
     const int tid = threadIdx.x;
@@ -155,6 +179,43 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         b_off[i] = (uint32_t)min(col, N - 1) * src_row_bytes + (uint32_t)c * 16u;
         b_k8[i] = c * 8;
     }
+    // K-row operands: a load instruction fills 1 KB = KR_RPI rows of a
+    // [64][BX] tile (BX / 8 chunks per row); lane l serves tile row
+    // KR_RPI q + l / (BX / 8) and physical chunk l % (BX / 8), the logical
+    // chunk (l % (BX / 8)) ^ 4 (row % 4).  The XOR moves the four rows a
+    // 16-lane group reads to four different 64-byte blocks of a 256-byte bank
+    // sweep (see read_frags).  Columns past the operand's last one are
+    // clamped to it (never stored); K rows at or past klim load zeros.
+    constexpr int A_CPR = BM / 8, B_CPR = BN / 8;      // chunks per K row
+    constexpr int A_RPI = 64 / A_CPR, B_RPI = 64 / B_CPR;  // K rows per instruction
+    int a_kr[AKR ? A_LD : 1], b_kr[BKR ? B_LD : 1];      // tile K row of the lane
+    uint32_t a_colb[AKR ? A_LD : 1], b_colb[BKR ? B_LD : 1];  // column byte offset
+    if constexpr (AKR) {
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int kr = (wid * A_LD + i) * A_RPI + lane / A_CPR;
+            const int c = (lane % A_CPR) ^ (4 * (kr & 3));
+            a_kr[i] = kr;
+            a_colb[i] = (uint32_t)(t.row0 + min(8 * c, rows - 8)) * 2u;
+        }
+    }
+    if constexpr (BKR) {
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int kr = (wid * B_LD + i) * B_RPI + lane / B_CPR;
+            const int c = (lane % B_CPR) ^ (4 * (kr & 3));
+            b_kr[i] = kr;
+            b_colb[i] = (uint32_t)(n0 + min(8 * c, N - n0 - 8)) * 2u;
+        }
+    }
+    // (descriptors are built per load from a selected base and size: a select
+    // between descriptor values is lowered through scratch memory)
+    const uint32_t a_rowb = (uint32_t)t.a_stride * 2u, b_rowb = (uint32_t)t.b_stride * 2u;
+    const int64_t akr_bytes = AKR ? (int64_t)t.klim * t.a_stride * 2 : 0;
+    const int b1_rows = min(t.b_split, t.klim);
+    const int64_t bkr1_bytes = BKR ? (int64_t)b1_rows * t.b_stride * 2 : 0;
+    const int64_t bkr3_bytes = BKR && t.B3 ? (int64_t)(t.klim - b1_rows) * t.b_stride * 2 : 0;
+    const uint16_t* bkr3_base = t.B3 ? t.B3 : t.B1;
     const int k_end = t.k_end;
     // Loads of K step kt into stage `st`.  A step past the end goes through a
     // zero-size resource: every load is out of range and writes zeros, so the
@@ -167,21 +228,48 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         const __amdgpu_buffer_rsrc_t ars = live ? a_rs : null_rs;
         const __amdgpu_buffer_rsrc_t brs1 = live ? b1_rs : null_rs;
         const __amdgpu_buffer_rsrc_t brs3 = live ? b3_rs : null_rs;
+        const int krow = t.krow0 + (live ? kt : 0) * BK;  // K row of tile row 0
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
-            const uint32_t off = KTAIL && k0 + a_k8[i] >= Kdim ? 0x80000000u : a_off[i];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ars, (__attribute__((address_space(3))) void*)(st + a_lrow(i) * ROW_BYTES), 16,
-                off, kb, 0, 0);
+            if constexpr (AKR) {
+                const int r = krow + a_kr[i];
+                const uint32_t off =
+                    r < t.klim ? (uint32_t)r * a_rowb + a_colb[i] : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc(t.A, live ? akr_bytes : 0),
+                    (__attribute__((address_space(3))) void*)(st + (wid * A_LD + i) * 1024), 16,
+                    off, 0, 0, 0);
+            } else {
+                const uint32_t off = KTAIL && k0 + a_k8[i] >= Kdim ? 0x80000000u : a_off[i];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ars, (__attribute__((address_space(3))) void*)(st + a_lrow(i) * ROW_BYTES),
+                    16, off, kb, 0, 0);
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
-            const uint32_t off = KTAIL && k0 + b_k8[i] >= Kdim ? 0x80000000u : b_off[i];
-            const bool second = GATEUP && i >= B_LD / 2;  // compile-time
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                second ? brs3 : brs1,
-                (__attribute__((address_space(3))) void*)(st + A_BYTES + b_lrow(i) * ROW_BYTES),
-                16, off, kb, 0, 0);
+            if constexpr (BKR) {
+                // the instruction's first row decides B1 or B3 (b_split is a
+                // multiple of the rows per instruction)
+                const int r0 = krow + (wid * B_LD + i) * B_RPI;
+                const bool in3 = r0 >= t.b_split;
+                const int r = krow + b_kr[i] - (in3 ? t.b_split : 0);
+                const int lim = in3 ? t.klim - t.b_split : b1_rows;
+                const uint32_t off = r < lim ? (uint32_t)r * b_rowb + b_colb[i] : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc(in3 ? bkr3_base : t.B1, live ? (in3 ? bkr3_bytes : bkr1_bytes) : 0),
+                    (__attribute__((address_space(3))) void*)(st + A_BYTES +
+                                                              (wid * B_LD + i) * 1024),
+                    16, off, 0, 0, 0);
+            } else {
+                const uint32_t off = KTAIL && k0 + b_k8[i] >= Kdim ? 0x80000000u : b_off[i];
+                const bool second = GATEUP && i >= B_LD / 2;  // compile-time
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    second ? brs3 : brs1,
+                    (__attribute__((address_space(3))) void*)(st + A_BYTES +
+                                                              b_lrow(i) * ROW_BYTES),
+                    16, off, kb, 0, 0);
+            }
         }
     };
 
@@ -210,15 +298,51 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // K-row fragments: lane l = 16 g + i16 of fragment f (32 columns from
+    // wave column c0 + 32 f) points at tile row 8 (g / 2) + i16 / 4 (+ 16 kk,
+    // + 4 for the second read) and column c0 + 32 f + 16 (g % 2) + 4 (i16 % 4),
+    // so lane l receives column c0 + 32 f + l % 32 at K rows 16 kk + 8 (l / 32)
+    // + 0..7.  Row % 4 = i16 / 4, so the swizzle is the lane's own constant.
+    // The 32 lanes of a half wave read 4 rows x 64 bytes, one 64-byte block
+    // per row, spread over a 256-byte bank sweep by the swizzle.
+    auto kr_off = [&](int c0, int f, int pitch) {
+        const int g = lane >> 4, i16 = lane & 15;
+        const int row = 8 * (g >> 1) + (i16 >> 2);
+        const int chunk = ((c0 + 32 * f) >> 3) + 2 * (g & 1) + ((i16 & 3) >> 1);
+        return (uint32_t)(row * pitch + ((chunk ^ (4 * (row & 3))) << 4) + (i16 & 1) * 8);
+    };
+    constexpr int A_PITCH = BM * 2, B_PITCH = BN * 2;
+    uint32_t a_fr[AKR ? TM : 1], b_fr[BKR ? TN : 1];
+    if constexpr (AKR) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a_fr[i] = kr_off(wm * WTM, i, A_PITCH);
+    }
+    if constexpr (BKR) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b_fr[j] = A_BYTES + kr_off(wn * WTN, j, B_PITCH);
+    }
+    auto tr_frag = [](const uint8_t* p, int pitch) {
+        const v4i16_t lo = lds_read_tr(p), hi = lds_read_tr(p + 4 * pitch);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto read_frags = [&](const uint8_t* st, int kk, bf16x8_t(&av)[TM], bf16x8_t(&bv)[TN]) {
         const uint8_t* pa = st + a_rd + kofs[kk];
         const uint8_t* pb = st + b_rd + kofs[kk];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            av[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pa + i * 32 * ROW_BYTES));
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (AKR)
+                av[i] = tr_frag(st + a_fr[i] + kk * 16 * A_PITCH, A_PITCH);
+            else
+                av[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pa + i * 32 * ROW_BYTES));
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bv[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pb + b_frag_row(j) * ROW_BYTES));
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (BKR)
+                bv[j] = tr_frag(st + b_fr[j] + kk * 16 * B_PITCH, B_PITCH);
+            else
+                bv[j] = as_bf16x8(
+                    *reinterpret_cast<const u32x4_t*>(pb + b_frag_row(j) * ROW_BYTES));
+        }
     };
     auto mfmas = [&](const bf16x8_t(&av)[TM], const bf16x8_t(&bv)[TN]) {
 #pragma unroll
@@ -233,11 +357,15 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // start of a sub-step, so their latency hides behind the remaining MFMAs;
     // the first sub-step of a step also carries the next step's loads (LPM
     // per MFMA).
+    constexpr int NRD = (AKR ? 2 : 1) * TM + (BKR ? 2 : 1) * TN;  // LDS reads per sub-step
     auto interleave = [&](int nloads) {
         constexpr int LPM = (NLD + TM * TN - 1) / (TM * TN);
+        constexpr int RPM = (NRD + TM * TN - 1) / (TM * TN);
 #pragma unroll
         for (int q = 0; q < TM * TN; ++q) {
-            if (q < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int r = 0; r < RPM; ++r)
+                if (q * RPM + r < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
             for (int r = 0; r < LPM; ++r)
                 if (q * LPM + r < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -359,13 +487,15 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     }
 }
 
-template <bool GATEUP, bool KTAIL, int NWV, int EPI>
+// BKR (plain products only): B1 / B3 are K-row weights [n][b_split][N]; K
+// rows [0, b_split) of the product come from B1_e, [b_split, Kdim) from B3_e.
+template <bool GATEUP, bool KTAIL, int NWV, int EPI, bool BKR = false>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
                       int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
-                      int64_t split_stride) {
+                      int64_t split_stride, int b_split = 0) {
     // gate/up also runs wide tiles (larger stages)
     using SQ = Square<NWV>;
     using WD = Wide<NWV>;
@@ -434,8 +564,17 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     t.A_src_rows = A_src_rows;
     t.perm = perm;
     t.K = K;
-    t.B1 = B1 + (int64_t)e * N * Kdim;
-    t.B3 = GATEUP ? B3 + (int64_t)e * N * Kdim : nullptr;
+    if constexpr (BKR) {
+        t.B1 = B1 + (int64_t)e * b_split * N;
+        t.B3 = B3 ? B3 + (int64_t)e * b_split * N : nullptr;
+        t.b_stride = N;
+        t.krow0 = 0;
+        t.klim = Kdim;
+        t.b_split = B3 ? b_split : Kdim;
+    } else {
+        t.B1 = B1 + (int64_t)e * N * Kdim;
+        t.B3 = GATEUP ? B3 + (int64_t)e * N * Kdim : nullptr;
+    }
     t.Kdim = Kdim;
     t.N = N;
     t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP ? 2 : 4);
@@ -448,7 +587,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         t.row0 = start + mt * SQ::BM;
         t.rows = min(SQ::BM, end - t.row0);
         t.n0 = (2 * c + L / gm) * BNO_S;
-        tile_body<GATEUP, KTAIL, SQ, STG, EPI>(t, S0, S1);
+        tile_body<GATEUP, KTAIL, SQ, STG, EPI, false, BKR>(t, S0, S1);
     } else if constexpr (WIDE_MAX > 0) {
         t.row0 = start + nsq * SQ::BM;
         t.rows = end - t.row0;
@@ -485,15 +624,16 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
 }
 
 // Weight gradients of the grouped products.  For every expert e,
-//   C_e[r][c] = sum over the expert's assignments p of A[r][p] B[c][p],
-// where A [N1][Kp] and B [N2][Kp] hold transposed activations whose columns
-// are the assignments in expert order, each expert's run zero-padded to a
-// multiple of 64 columns (padded offsets poff).  A tile of C_e is a K range
-// of the same square tile body (fp32 out); C_e = C + e N1 N2.
+//   C_e[r][c] = sum over the expert's assignment rows p of A[p][r] B[p][c],
+// with A [A_rows][a_stride] and B [A_rows][b_stride] in expert order (rows
+// offsets[e] .. offsets[e+1] - 1 of both): a product over K rows, both
+// operands K-row (no transposed copies).  C_e = C + e N1 N2, fp32, every
+// element written (zero for an expert without rows).
 template <int NWV>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
-void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                       const int32_t* __restrict__ offsets, int n, int Kp, int N1, int N2,
+void gemm_wgrad_kernel(const uint16_t* __restrict__ A, int64_t a_stride,
+                       const uint16_t* __restrict__ B, int64_t b_stride,
+                       const int32_t* __restrict__ offsets, int n, int N1, int N2,
                        float* __restrict__ C) {
     using SQ = Square<NWV>;
     constexpr int STG = SQ::STAGE_BYTES;
@@ -509,26 +649,29 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
     const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
     if (jx >= per_xcd || L0 >= tiles) return;
     const int e = L0 / per_e, rem = L0 - e * per_e;
-    int pbeg = 0;
-    for (int q = 0; q < e; ++q) pbeg += (offsets[q + 1] - offsets[q] + BK - 1) / BK * BK;
-    const int pend = pbeg + (offsets[e + 1] - offsets[e] + BK - 1) / BK * BK;
+    const int pbeg = offsets[e], pend = offsets[e + 1];
     TileArgs t;
     t.A = A;
-    t.A_src_rows = N1;
+    t.A_src_rows = 0;
     t.perm = nullptr;
     t.K = 1;
     t.B1 = B;
     t.B3 = nullptr;
-    t.Kdim = Kp;
+    t.Kdim = 0;
     t.N = N2;
     t.Cout = C + (int64_t)e * N1 * N2;
     const int mt = rem % mtn, nt = rem / mtn;
     t.row0 = mt * SQ::BM;
     t.rows = min(SQ::BM, N1 - t.row0);
     t.n0 = nt * SQ::BN;
-    t.k_begin = pbeg / BK;
-    t.k_end = pend / BK;
-    tile_body<false, false, SQ, STG, 0>(t, S0, S1);
+    t.k_begin = 0;
+    t.k_end = (pend - pbeg + BK - 1) / BK;
+    t.a_stride = a_stride;
+    t.b_stride = b_stride;
+    t.krow0 = pbeg;
+    t.klim = pend;
+    t.b_split = pend;
+    tile_body<false, false, SQ, STG, 0, true, true>(t, S0, S1);
 }
 
 }  // namespace
@@ -593,16 +736,40 @@ hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, con
                                     AB, 8, 1, s);
 }
 
-hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* offsets,
-                                  int n, int Kp, int N1, int N2, float* C, hipStream_t s) {
-    if (Kp % BK != 0 || (int64_t)N1 * Kp * 2 >= (int64_t(1) << 31) ||
-        (int64_t)N2 * Kp * 2 >= (int64_t(1) << 31))
+hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uint16_t* B,
+                                  int64_t b_stride, const int32_t* offsets, int n,
+                                  int64_t A_rows, int N1, int N2, float* C, hipStream_t s) {
+    const int64_t lim = int64_t(1) << 31;
+    if (N1 % 8 || N2 % 8 || A_rows * a_stride * 2 >= lim || A_rows * b_stride * 2 >= lim)
         return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)n * ((N1 + 255) / 256) * ((N2 + 255) / 256);
     const int64_t blocks = (tiles + 7) / 8 * 8;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_wgrad_kernel<8>), dim3((unsigned)blocks), dim3(512), 0, s, A, B,
-                       offsets, n, Kp, N1, N2, C);
+    hipLaunchKernelGGL((gemm_wgrad_kernel<8>), dim3((unsigned)blocks), dim3(512), 0, s, A,
+                       a_stride, B, b_stride, offsets, n, N1, N2, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
+                                 const uint16_t* B3, int b_split, const int32_t* offsets, int n,
+                                 int Kdim, int N, float* C, int splits, hipStream_t s) {
+    const int64_t lim = int64_t(1) << 31;
+    if (N % 8 || Kdim % 8 || (B3 ? 2 * b_split != Kdim : b_split != Kdim) ||
+        A_rows * Kdim * 2 >= lim || (int64_t)b_split * N * 2 >= lim || splits < 1)
+        return hipErrorInvalidValue;
+    using SQ = Square<8>;
+    const int64_t mslots = A_rows / SQ::BM + n;
+    const int64_t blocks = (mslots * ((N + SQ::BN - 1) / SQ::BN) * splits + 7) / 8 * 8;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t stride = A_rows * (int64_t)N;
+    if (Kdim % BK)
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, true, 8, 0, true>), dim3((unsigned)blocks),
+                           dim3(512), 0, s, A, A_rows, nullptr, 1, B1, B3, offsets, n, Kdim, N,
+                           (void*)C, 8, splits, stride, b_split);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 8, 0, true>), dim3((unsigned)blocks),
+                           dim3(512), 0, s, A, A_rows, nullptr, 1, B1, B3, offsets, n, Kdim, N,
+                           (void*)C, 8, splits, stride, b_split);
     return hipGetLastError();
 }
 

@@ -35,11 +35,19 @@ hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, con
                                       int K, const uint16_t* B1, const uint16_t* B3,
                                       const int32_t* offsets, int n, int64_t A_rows, int Kdim,
                                       int N, uint16_t* AB, hipStream_t s);
-// Per-expert weight gradients C_e[N1][N2] = A_e B_e^T over the expert's
-// assignments: A [N1][Kp], B [N2][Kp] bf16, columns in expert order, each
-// expert's run zero-padded to a multiple of 64; fp32 out, C_e = C + e N1 N2.
-hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* offsets,
-                                  int n, int Kp, int N1, int N2, float* C, hipStream_t s);
+// Per-expert weight gradients C_e[r][c] = sum over the expert's rows p of
+// A[p][r] B[p][c] (A, B bf16 in expert order, row strides a_stride,
+// b_stride); fp32 out, C_e = C + e N1 N2, zero for an expert without rows.
+hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uint16_t* B,
+                                  int64_t b_stride, const int32_t* offsets, int n,
+                                  int64_t A_rows, int N1, int N2, float* C, hipStream_t s);
+// C[s][p][c] (fp32, row stride N, split stride A_rows N) = sum over the K
+// range of split s of A[p][k] W_e[k][c], over the rows p of each expert e,
+// with K-row weights: W_e = B1 + e b_split N for k < b_split and
+// B3 + e b_split N (row k - b_split) beyond (B3 NULL: Kdim = b_split).
+hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
+                                 const uint16_t* B3, int b_split, const int32_t* offsets, int n,
+                                 int Kdim, int N, float* C, int splits, hipStream_t s);
 // K splits worth using for the tiled down projection on `cus` compute units
 // (at most min(max_splits, 4)): the count that minimises tile rounds per split
 // plus the cost of the extra fp32 partial sums.  Depends on sizes only.
@@ -67,31 +75,26 @@ hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int 
                           const void* x, void* y, hipStream_t s);
 
 // ---- backward pass (backward.hip) ---------------------------------------------
-// H = bf16(SiLU(a) b) from rows [a | b].
-hipError_t launch_bwd_h(const uint16_t* AB, int64_t A, int dff, uint16_t* H, hipStream_t s);
-// dg[a] = dy_t . O[p], DO[p] = bf16(gate[a] dy_t) for a = perm[p], t = a / K.
-hipError_t launch_bwd_gates(const uint16_t* dy, const float* O, const int32_t* perm,
-                            const float* gate, int64_t A, int K, int d, float* dg, uint16_t* DO,
-                            hipStream_t s);
-// [da | db] (bf16) from [a | b] and the fp32 gradient of h.
-hipError_t launch_bwd_swiglu(const uint16_t* AB, const float* DH, int64_t A, int dff,
-                             uint16_t* DADB, hipStream_t s);
-// Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j DX[inv[t K + j]].
+// Per assignment row p (a = perm[p]) from [a | b] = AB[p] and the fp32
+// gradient DH[p] of h with respect to the ungated expert output (W2_e^T dy):
+// dg[a] = h . DH[p] (h = bf16(SiLU(a) b)), DADB[p] = [da | db] of the gated
+// gradient gate[a] DH[p], GH[p] = bf16(gate[a] h).
+hipError_t launch_bwd_swiglu(const uint16_t* AB, const float* DH, const int32_t* perm,
+                             const float* gate, int64_t A, int dff, float* dg, uint16_t* DADB,
+                             uint16_t* GH, hipStream_t s);
+// Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j sum_s
+// DX[s][inv[t K + j]] (S K-split partials, split stride A d).
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,
-                            const float* dg, const float* DX, const int32_t* inv, int64_t T,
-                            int K, int n, int d, float* dl, uint16_t* dx, hipStream_t s);
+                            const float* dg, const float* DX, int S, int64_t A,
+                            const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
+                            uint16_t* dx, hipStream_t s);
 // dW_g = sum_t x_t dl_t^T via fixed-order partial sums (part: chunks x d x n).
 int bwd_dwg_chunks(int64_t T);
 hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, int n,
                           float* part, float* dwg, hipStream_t s);
-// Batched transpose: out[c][ooff + r] = in[r][icol0 + c].
-hipError_t launch_transpose(const uint16_t* in, int64_t R, int C, int64_t istride, int icol0,
-                            int64_t ibatch, uint16_t* out, int64_t ostride, int64_t ooff,
-                            int64_t obatch, int batches, hipStream_t s);
-// Expert-padded transpose of assignment rows (optionally gathered through
-// perm / K) into out[C][Kp].
-hipError_t launch_transpose_pad(const uint16_t* in, int C, int64_t istride, int icol0,
-                                const int32_t* offsets, int n, const int32_t* perm, int K,
-                                int64_t Kp, uint16_t* out, hipStream_t s);
+// XG[p] = x[perm[p] / K] and YG[p] = y[perm[p] / K] (bf16 rows of d
+// elements), p < A.
+hipError_t launch_gather_rows(const uint16_t* x, const uint16_t* y, const int32_t* perm, int K,
+                              int64_t A, int d, uint16_t* XG, uint16_t* YG, hipStream_t s);
 
 }  // namespace moe
