@@ -322,8 +322,8 @@ def bench_backward(args, w, dev):
         "config": {"workload": w.name + "-backward", "T": w.T, "d": w.d, "d_ff": w.d_ff,
                    "n": w.n, "K": w.K, "dtype": w.dtype},
         "roofline": roof,
-        # forward recompute 6, dh 2, dx 4, weight gradients 6 (x A d d_ff)
-        "step_tflops": round(18.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12, 1),
+        # gate/up recompute 4, r = W2^T dy 2, dx 4, weight gradients 6 (x A d d_ff)
+        "step_tflops": round(16.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12, 1),
         "counts": counts,
     }
     if args.cpu_budget > 0:

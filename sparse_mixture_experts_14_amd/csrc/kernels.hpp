@@ -40,7 +40,8 @@ hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, con
 // b_stride); fp32 out, C_e = C + e N1 N2, zero for an expert without rows.
 hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uint16_t* B,
                                   int64_t b_stride, const int32_t* offsets, int n,
-                                  int64_t A_rows, int N1, int N2, float* C, hipStream_t s);
+                                  int64_t A_rows, int N1, int N2, float* C, int GM,
+                                  hipStream_t s);
 // C[s][p][c] (fp32, row stride N, split stride A_rows N) = sum over the K
 // range of split s of A[p][k] W_e[k][c], over the rows p of each expert e,
 // with K-row weights: W_e = B1 + e b_split N for k < b_split and
