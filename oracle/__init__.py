@@ -75,6 +75,9 @@ def _load():
     lib.oracle_backward.restype = ctypes.c_int
     lib.oracle_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32,
                                     P, I64, P, P, P, P, P, P]
+    lib.oracle_backward_entries.restype = ctypes.c_int
+    lib.oracle_backward_entries.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32, P,
+                                            I64, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -235,3 +238,38 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, rows=None, forced=None, weights: boo
     if rc != 0:
         raise ValueError(f"oracle_backward failed (rc={rc})")
     return out
+
+
+_WHICH = {"dW1": 1, "dW2": 2, "dW3": 3}
+
+
+def backward_entries(x, Wg, W1, W3, W2, dy, K: int, entries, forced=None) -> np.ndarray:
+    """Selected expert weight-gradient entries (fp64), each summed over all the
+    tokens routed to its expert.  ``entries``: sequence of (name, e, row, col)
+    with name in dW1 / dW2 / dW3 and (row, col) indices of that matrix of
+    expert e.  ``forced`` ([T][K]) replaces TopK."""
+    x = _f32(x)
+    Wg = _f32(Wg)
+    W1 = _f32(W1)
+    W3 = _f32(W3)
+    W2 = _f32(W2)
+    dy = _f32(dy)
+    T, d = x.shape
+    n = Wg.shape[1]
+    d_ff = W1.shape[1]
+    Q = len(entries)
+    which = np.ascontiguousarray([_WHICH[q[0]] for q in entries], dtype=np.int32)
+    ex = np.ascontiguousarray([q[1] for q in entries], dtype=np.int32)
+    ri = np.ascontiguousarray([q[2] for q in entries], dtype=np.int64)
+    ci = np.ascontiguousarray([q[3] for q in entries], dtype=np.int64)
+    forced_a = None
+    if forced is not None:
+        forced_a = np.ascontiguousarray(np.asarray(forced, dtype=np.int32))
+        assert forced_a.shape == (T, K)
+    out = np.empty(max(Q, 1), np.float64)
+    rc = _load().oracle_backward_entries(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2),
+                                         _ptr(dy), T, d, d_ff, n, K, _ptr(forced_a), Q,
+                                         _ptr(which), _ptr(ex), _ptr(ri), _ptr(ci), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_backward_entries failed (rc={rc})")
+    return out[:Q]

@@ -523,3 +523,96 @@ int oracle_backward(const float* x, const float* Wg, const float* W1, const floa
     free(keep_sel);
     return 0;
 }
+
+/* Selected entries of the expert weight gradients, for checks at sizes where
+ * the full gradients are out of reach.  Each entry is summed over every token
+ * routed to its expert, in token order, from the per-token definition above
+ * restricted to the one hidden unit f the entry needs:
+ *   a_f = W1_e[f] . x,  b_f = W3_e[f] . x,  h_f = SiLU(a_f) b_f,
+ *   r_f = sum_c W2_e[c][f] dy[c]  (the f-th entry of W2_e^T dy),
+ *   dh_f = g_j r_f,  da_f = dh_f b_f SiLU'(a_f),  db_f = dh_f SiLU(a_f);
+ *   dW2_e[c][f] = sum g_j dy[c] h_f,  dW1_e[f][k] = sum da_f x[k],
+ *   dW3_e[f][k] = sum db_f x[k].
+ * Entry q: which[q] = 1 (dW1), 2 (dW2) or 3 (dW3), expert ex[q], row ri[q]
+ * and column ci[q] of that matrix.  Routing: forced[T][K] if given, else
+ * TopK.  out[Q] in fp64.  Returns 0, -1 on invalid arguments, -2 on
+ * allocation failure. */
+int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
+                            const float* W3, const float* W2, const float* dy, int64_t T,
+                            int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                            const int32_t* forced, int64_t Q, const int32_t* which,
+                            const int32_t* ex, const int64_t* ri, const int64_t* ci,
+                            double* out) {
+    if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n || Q < 0)
+        return -1;
+    for (int64_t q = 0; q < Q; ++q) {
+        if (which[q] < 1 || which[q] > 3 || ex[q] < 0 || ex[q] >= n) return -1;
+        const int64_t rows = which[q] == 2 ? d : d_ff, cols = which[q] == 2 ? d_ff : d;
+        if (ri[q] < 0 || ri[q] >= rows || ci[q] < 0 || ci[q] >= cols) return -1;
+    }
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    double* gate = (double*)malloc(sizeof(double) * ((size_t)T * K + 1));
+    if (!sel || !gate) {
+        free(sel);
+        free(gate);
+        return -2;
+    }
+    /* routing and gates of every token */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double l[64], g[64];
+        int32_t s[64];
+        for (int32_t i = 0; i < n; ++i) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < d; ++k)
+                acc += (double)x[t * d + k] * (double)Wg[k * n + i];
+            l[i] = acc;
+        }
+        if (forced) {
+            for (int32_t j = 0; j < K; ++j) s[j] = forced[t * K + j];
+        } else {
+            topk_select(l, n, K, s);
+        }
+        masked_softmax(l, s, K, g);
+        for (int32_t j = 0; j < K; ++j) {
+            sel[t * K + j] = s[j];
+            gate[t * K + j] = g[j];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < Q; ++q) {
+        const int64_t e = ex[q];
+        const int64_t f = which[q] == 2 ? ci[q] : ri[q];  /* hidden unit */
+        const float* w1 = W1 + (e * d_ff + f) * d;
+        const float* w3 = W3 + (e * d_ff + f) * d;
+        const float* w2 = W2 + e * d * d_ff;
+        double s = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t j = 0; j < K; ++j) {
+                if (sel[t * K + j] != e) continue;
+                const float* xt = x + t * d;
+                const float* dyt = dy + t * d;
+                const double g = gate[t * K + j];
+                double a = 0.0, b = 0.0;
+                for (int64_t k = 0; k < d; ++k) {
+                    a += (double)w1[k] * (double)xt[k];
+                    b += (double)w3[k] * (double)xt[k];
+                }
+                if (which[q] == 2) {
+                    s += g * (double)dyt[ri[q]] * (silu(a) * b);
+                    continue;
+                }
+                double r = 0.0;
+                for (int64_t c = 0; c < d; ++c) r += (double)w2[c * d_ff + f] * (double)dyt[c];
+                const double dh = g * r;
+                const double sg = 1.0 / (1.0 + exp(-a));
+                const double unit = which[q] == 1 ? dh * b * (sg + a * sg * (1.0 - sg))
+                                                  : dh * a * sg;
+                s += unit * (double)xt[ci[q]];
+            }
+        out[q] = s;
+    }
+    free(sel);
+    free(gate);
+    return 0;
+}

@@ -81,7 +81,8 @@ def test_backward_small(T, d, d_ff, n, K, seed):
 
 def test_backward_tile_boundaries_and_empty_expert():
     # K = 1 with steered routing: experts get 128, 129, 255, 256, 257, 384, 385
-    # and 0 rows, across the 64-row padding of the weight-gradient products
+    # and 0 rows: K ranges of the weight-gradient products that start and end
+    # inside a 64-row step, and an expert with none
     sizes = [128, 129, 255, 256, 257, 384, 385, 0]
     L, _ = steered_layer(sizes, 256, 328, seed=31)
     _, counts = check_backward(L, 1, _dy(sum(sizes), 256, 131), "tile-boundaries")
@@ -108,3 +109,49 @@ def test_backward_no_tokens_zeroes_weight_gradients():
     torch.cuda.synchronize()
     for name in ("dWg", "dW1", "dW3", "dW2"):
         assert not torch.any(got[name]), name
+
+
+def test_backward_prefill_size_sampled():
+    # the prefill workload (T = 4096, Mixtral widths) with the output gradient
+    # the benchmark draws, in the launch configuration it times: routing on
+    # every token, dx on sampled tokens, sampled entries of every expert's
+    # weight gradients (each a sum over all the expert's tokens), and the
+    # zero row sums of dW_g
+    from sparse_mixture_experts_14_amd import workloads as W
+    w = W.WORKLOADS["prefill"]
+    L = W.make_layer(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    dy = torch.randn(w.T, w.d, generator=g, device="cuda").to(torch.bfloat16)
+    say(f"[case] backward prefill-size T={w.T} d={w.d} d_ff={w.d_ff} n={w.n} K={w.K}")
+    got = moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K)
+    gi, gg = moe.route(L["x"], L["Wg"], w.K)
+    torch.cuda.synchronize()
+    H = host_inputs(L)
+    gi, gg = P.to_np(gi), P.to_np(gg)
+    lg, oi, og = oracle.route(H["x"], H["Wg"], w.K)
+    rep = P.routing_report(gi, gg, lg, oi, og, w.K)
+    assert not rep["bad"], f"routing mismatch on tokens {rep['bad'][:10]}"
+    dyh = P.to_np(dy.float())
+    rng = np.random.default_rng(77)
+    rows = np.sort(rng.choice(w.T, 8, replace=False))
+    ref = oracle.backward(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], dyh, w.K, rows=rows,
+                          forced=gi[rows])
+    errs = {"dx": P.rel_l2(P.to_np(got["dx"].float())[rows], ref["dx"])}
+    ents = []
+    for q in range(48):
+        name = ("dW1", "dW2", "dW3")[q % 3]
+        nr, nc = (w.d, w.d_ff) if name == "dW2" else (w.d_ff, w.d)
+        ents.append((name, q % w.n, int(rng.integers(nr)), int(rng.integers(nc))))
+    want = oracle.backward_entries(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], dyh, w.K, ents,
+                                   forced=gi)
+    have = np.array([got[nm][e, i, j].item() for nm, e, i, j in ents])
+    for name in ("dW1", "dW2", "dW3"):
+        sel = [q for q, en in enumerate(ents) if en[0] == name]
+        errs[name] = P.rel_l2(have[sel], want[sel])
+    rs = got["dWg"].double().sum(1).abs().max().item()
+    scale = got["dWg"].double().abs().max().item()
+    say("       " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
+        f" near_ties={rep['near_ties']} dWg_rowsum={rs:.1e}/{scale:.1e}")
+    for name, e in errs.items():
+        assert e <= P.TOL_BF16, f"{name}: rel L2 {e} > {P.TOL_BF16}"
+    assert scale > 0 and rs <= 1e-5 * scale * w.n

@@ -134,3 +134,52 @@ def test_zero_output_gradient():
     g = oracle.backward(x, Wg, W1, W3, W2, np.zeros((5, 8), np.float32), 2)
     for v in g.values():
         assert not np.any(v)
+
+
+def _entries(rng, n, d, d_ff, count):
+    """(name, e, row, col) samples over the three expert weight gradients."""
+    out = []
+    for q in range(count):
+        name = ("dW1", "dW2", "dW3")[q % 3]
+        rows, cols = (d, d_ff) if name == "dW2" else (d_ff, d)
+        out.append((name, int(rng.integers(n)), int(rng.integers(rows)),
+                    int(rng.integers(cols))))
+    return out
+
+
+def test_backward_entries_match_dense_autograd():
+    # sampled weight-gradient entries of the K = n dense mixture against torch
+    # fp64 autograd (an independent chain rule)
+    rng = np.random.default_rng(11)
+    T, d, d_ff, n = 9, 8, 12, 4
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    X = _t64(x)
+    G = _t64(Wg)
+    A1, A3, A2 = (_t64(w).requires_grad_() for w in (W1, W3, W2))
+    gates = torch.softmax(X @ G, dim=1)
+    h = F.silu(torch.einsum("td,efd->tef", X, A1)) * torch.einsum("td,efd->tef", X, A3)
+    Y = (gates[:, :, None] * torch.einsum("tef,ecf->tec", h, A2)).sum(1)
+    (Y * _t64(dy)).sum().backward()
+    ref = {"dW1": A1.grad.numpy(), "dW3": A3.grad.numpy(), "dW2": A2.grad.numpy()}
+    ents = _entries(rng, n, d, d_ff, 30)
+    got = oracle.backward_entries(x, Wg, W1, W3, W2, dy, n, ents)
+    want = np.array([ref[nm][e, i, j] for nm, e, i, j in ents])
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_backward_entries_match_full_backward():
+    # routed top-2 case: the per-entry sums equal the full backward's entries
+    rng = np.random.default_rng(12)
+    T, d, d_ff, n = 40, 16, 24, 8
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    full = oracle.backward(x, Wg, W1, W3, W2, dy, 2)
+    ents = _entries(rng, n, d, d_ff, 60)
+    got = oracle.backward_entries(x, Wg, W1, W3, W2, dy, 2, ents)
+    want = np.array([full[nm][e, i, j] for nm, e, i, j in ents])
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-13)
+    # forced routing: the same as TopK when forced to TopK's own choice
+    _, idx, _, _ = oracle.forward(x, Wg, W1, W3, W2, 2)
+    got_f = oracle.backward_entries(x, Wg, W1, W3, W2, dy, 2, ents, forced=idx)
+    assert np.array_equal(got_f, got)

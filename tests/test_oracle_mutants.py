@@ -58,7 +58,18 @@ BACKWARD_MUTANTS = {
                           "if (dW1) dW1[(e * d_ff + f) * d + k] = s3;"),
 }
 
+# Mistakes in the per-entry weight gradients (oracle_backward_entries).
+BACKWARD_MUTANTS.update({
+    "entries_silu_derivative": ("dh * b * (sg + a * sg * (1.0 - sg))", "dh * b * sg"),
+    "entries_gate_dropped": ("s += g * (double)dyt[ri[q]] * (silu(a) * b);",
+                             "s += (double)dyt[ri[q]] * (silu(a) * b);"),
+    "entries_w2_transposed": ("r += (double)w2[c * d_ff + f] * (double)dyt[c];",
+                              "r += (double)w2[f * d + c] * (double)dyt[c];"),
+})
+
 BACKWARD_PINS = [
+    lambda o: bpins.test_backward_entries_match_dense_autograd(),
+    lambda o: bpins.test_backward_entries_match_full_backward(),
     lambda o: bpins.test_backward_matches_finite_differences(),
     lambda o: bpins.test_single_expert_backward_is_swiglu_autograd(),
     lambda o: bpins.test_dense_mixture_backward_when_K_equals_n(),
