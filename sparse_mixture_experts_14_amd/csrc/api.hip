@@ -327,7 +327,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.DX = o;      o = align256(o + kBwdMaxSplits * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
     L.DYG = o;     o = align256(o + A * dd * 2);
-    L.DH = o;      o = align256(o + A * ff * 4);
+    L.DH = o;      o = align256(o + A * ff * 2);
     L.DADB = o;    o = align256(o + A * 2 * ff * 2);
     L.GH = o;      o = align256(o + A * ff * 2);
     L.XG = o;      o = align256(o + A * dd * 2);
@@ -404,7 +404,7 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     float* DX = static_cast<float*>(at(L.DX));
     float* dg = static_cast<float*>(at(L.dg));
     uint16_t* DYG = static_cast<uint16_t*>(at(L.DYG));
-    float* DH = static_cast<float*>(at(L.DH));
+    uint16_t* DH = static_cast<uint16_t*>(at(L.DH));
     uint16_t* DADB = static_cast<uint16_t*>(at(L.DADB));
     uint16_t* GH = static_cast<uint16_t*>(at(L.GH));
     uint16_t* XG = static_cast<uint16_t*>(at(L.XG));
@@ -428,6 +428,7 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         return true;
     };
     const int cus = device_cus();
+    // (the cost model's choice measured best: 4 splits at T = 4096)
     const int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
     // routing and the pre-activations [a | b] recomputed
     if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
@@ -442,15 +443,15 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
          "row gather");
     // r = dy W2_e (W2_e [d][d_ff] read as K rows), then per row: dg = h . r,
     // [da | db] of g r, g h
-    STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, 1, s),
+    STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, true, 1, s),
          "dh product");
     STEP(moe::launch_bwd_swiglu(AB, DH, perm, gate, A, F, dg, DADB, GH, s), "SwiGLU backward");
     if (!mark(g_ev_end[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
     // dx per assignment = da W1_e + db W3_e: K rows 0..d_ff-1 from W1_e, the
     // next d_ff from W3_e, against the rows [da | db]; K-split partials
-    STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, dx_splits,
-                                    s),
+    STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, false,
+                                    dx_splits, s),
          "dx product");
     // router gradient, dx back in token order, dW_g
     STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, dx_splits,

@@ -25,12 +25,12 @@ namespace {
 __device__ __forceinline__ float bf(uint16_t v) { return bf16_bits_to_f32(v); }
 
 // One block per assignment row p (a = perm[p], g = gate[a]); 8 elements of
-// [a | b] and of r = DH[p] per thread and step:
+// [a | b] and of r = DH[p] (bf16) per thread and step:
 //   h = bf16(SiLU(a) b) (the forward's rounding point), dg[a] = sum h r
 //   (fixed-order block sum), dh = g r, da = dh b SiLU'(a), db = dh SiLU(a),
 //   DADB[p] = bf16([da | db]), GH[p] = bf16(g h).
 __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
-    const uint16_t* __restrict__ AB, const float* __restrict__ DH,
+    const uint16_t* __restrict__ AB, const uint16_t* __restrict__ DH,
     const int32_t* __restrict__ perm, const float* __restrict__ gate, int dff,
     float* __restrict__ dg, uint16_t* __restrict__ DADB, uint16_t* __restrict__ GH) {
     __shared__ float part[4];
@@ -38,16 +38,15 @@ __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
     const int a_idx = perm[p];
     const float g = gate[a_idx];
     const uint16_t* ab = AB + p * 2 * dff;
-    const float* r = DH + p * dff;
+    const uint16_t* r = DH + p * dff;
     uint16_t* dadb = DADB + p * 2 * dff;
     float acc = 0.0f;
     for (int c = threadIdx.x * 8; c < dff; c += 256 * 8) {
         float av[8], bv[8], h[8], da[8], db[8], gh[8];
         unpack_bf16x8(*reinterpret_cast<const uint4*>(ab + c), av);
         unpack_bf16x8(*reinterpret_cast<const uint4*>(ab + dff + c), bv);
-        const float4 r0 = *reinterpret_cast<const float4*>(r + c);
-        const float4 r1 = *reinterpret_cast<const float4*>(r + c + 4);
-        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        float rv[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(r + c), rv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float sg = 1.0f / (1.0f + expf(-av[i]));
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
 
 // Per token: the router-logit gradient dl (thread 0, written to dl[t][n]),
 // then dx_t = W_g dl + sum_j sum_s DX[s][inv[t K + j]] in fp32 (in that
-// order), rounded once to bf16.
+// order), rounded once to bf16 (RNE).
 __global__ __launch_bounds__(256) void bwd_token_kernel(
     const uint16_t* __restrict__ wg, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const float* __restrict__ dg, const float* __restrict__ DX,
@@ -102,37 +101,76 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
     }
     __syncthreads();
     if (threadIdx.x < n) dl[t * n + threadIdx.x] = sdl[threadIdx.x];
-    for (int k = threadIdx.x; k < d; k += 256) {
-        float s = 0.0f;
-        for (int i = 0; i < n; ++i) s = fmaf(bf(wg[(int64_t)k * n + i]), sdl[i], s);
+    // four columns per thread: 16-byte loads of the partial sums
+    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+        float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < n; ++i) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[u] = fmaf(bf(wg[(int64_t)(k + u) * n + i]), sdl[i], s[u]);
+        }
         for (int j = 0; j < K; ++j) {
             const float* src = DX + (int64_t)inv[t * K + j] * d + k;
-            for (int q = 0; q < S; ++q) s += src[q * split_stride];
+            for (int q = 0; q < S; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(src + q * split_stride);
+                s[0] += v.x;
+                s[1] += v.y;
+                s[2] += v.z;
+                s[3] += v.w;
+            }
         }
-        dx[t * d + k] = (uint16_t)f32_to_bf16_bits(s);
+        uint2 o;
+        o.x = pack_bf16x2(s[0], s[1]);
+        o.y = pack_bf16x2(s[2], s[3]);
+        *reinterpret_cast<uint2*>(dx + t * d + k) = o;
     }
 }
 
 // dW_g partial sums: block (kb, ch) covers rows [256 kb, 256 kb + 256) of
-// W_g and tokens [ch tpc, (ch + 1) tpc); part[ch][k][i] = sum_t x[t][k] dl[t][i].
+// W_g and tokens [ch tpc, (ch + 1) tpc); part[ch][k][i] = sum_t x[t][k] dl[t][i]
+// in token order.  The block's dl rows go through LDS 64 tokens at a time,
+// padded to NE columns with zeros, and each thread keeps 8 independent x
+// loads in flight.
 template <int NE>
 __global__ __launch_bounds__(256) void bwd_dwg_partial_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ dl,
                                                              int64_t T, int d, int n, int tpc,
                                                              float* __restrict__ part) {
+    constexpr int TB = 64;  // tokens per LDS batch
+    __shared__ float sdl[TB][NE];
     const int k = blockIdx.x * 256 + threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.y * tpc;
     const int64_t t1 = min(T, t0 + tpc);
     float acc[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
-    if (k < d) {
-        for (int64_t t = t0; t < t1; ++t) {
-            const float xv = bf(x[t * d + k]);
-#pragma unroll
-            for (int i = 0; i < NE; ++i)
-                if (i < n) acc[i] = fmaf(xv, dl[t * n + i], acc[i]);
+    const uint16_t* xp = x + (k < d ? k : 0);
+    for (int64_t tb = t0; tb < t1; tb += TB) {
+        const int cnt = (int)min((int64_t)TB, t1 - tb);
+        __syncthreads();
+        for (int q = threadIdx.x; q < TB * NE; q += 256) {
+            const int tt = q / NE, i = q % NE;
+            sdl[tt][i] = (tt < cnt && i < n) ? dl[(tb + tt) * n + i] : 0.0f;
         }
+        __syncthreads();
+        if (k < d) {
+            int tt = 0;
+            for (; tt + 8 <= cnt; tt += 8) {
+                float xv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) xv[u] = bf(xp[(tb + tt + u) * d]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < NE; ++i) acc[i] = fmaf(xv[u], sdl[tt + u][i], acc[i]);
+            }
+            for (; tt < cnt; ++tt) {
+                const float xv = bf(xp[(tb + tt) * d]);
+#pragma unroll
+                for (int i = 0; i < NE; ++i) acc[i] = fmaf(xv, sdl[tt][i], acc[i]);
+            }
+        }
+    }
+    if (k < d) {
         float* o = part + ((int64_t)blockIdx.y * d + k) * n;
 #pragma unroll
         for (int i = 0; i < NE; ++i)
@@ -147,6 +185,7 @@ __global__ __launch_bounds__(256) void bwd_dwg_final_kernel(const float* __restr
     const int64_t q = blockIdx.x * 256ll + threadIdx.x;
     if (q >= dn) return;
     float s = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * dn + q];
     dwg[q] = s;
 }
@@ -177,7 +216,7 @@ unsigned grid_for(int64_t work, int64_t per_block) {
 
 }  // namespace
 
-hipError_t launch_bwd_swiglu(const uint16_t* AB, const float* DH, const int32_t* perm,
+hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const int32_t* perm,
                              const float* gate, int64_t A, int dff, float* dg, uint16_t* DADB,
                              uint16_t* GH, hipStream_t s) {
     if (A > 0x7fffffff || dff % 8) return hipErrorInvalidConfiguration;
@@ -196,7 +235,7 @@ hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float*
     return hipGetLastError();
 }
 
-int bwd_dwg_chunks(int64_t T) { return (int)((T + 255) / 256 < 64 ? (T + 255) / 256 : 64); }
+int bwd_dwg_chunks(int64_t T) { return (int)((T + 63) / 64 < 256 ? (T + 63) / 64 : 256); }
 
 hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, int n,
                           float* part, float* dwg, hipStream_t s) {

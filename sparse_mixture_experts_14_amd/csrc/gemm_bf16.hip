@@ -110,7 +110,8 @@ __device__ __forceinline__ v4i16_t lds_read_tr(const uint8_t* p) {
 // One output tile: loads, MFMA main loop and epilogue.  S0 and S1 are the two
 // LDS stages (separate objects, so the compiler can tell the stage being read
 // from the stage being filled).
-// EPI (gate/up only): 0 stores H = bf16(SiLU(a) * b); 1 stores the
+// EPI 2 (plain products): the fp32 sums are stored rounded to bf16.
+// EPI (gate/up): 0 stores H = bf16(SiLU(a) * b); 1 stores the
 // pre-activations themselves, a and b in bf16, as rows [a | b] of 2 N columns
 // (the backward pass needs them).
 // AKR / BKR: the A / B operand is a K-row operand ([K][M] / [K][N], rows of
@@ -427,7 +428,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // in its own LDS slot, padded by 16 bytes per row against bank
     // conflicts, and writes it back as whole 16-byte chunks of output rows.
     constexpr int OCOLS = GATEUP ? WTN / 2 : WTN;           // output columns per wave
-    constexpr int ES = GATEUP ? 2 : 4;                       // output element bytes
+    constexpr int ES = GATEUP || EPI == 2 ? 2 : 4;           // output element bytes
     constexpr int RSTRIDE = OCOLS * ES + 16;                 // LDS row stride (bytes)
     constexpr int SLOT = 32 * RSTRIDE;                       // one wave's staging slot
     static_assert(SLOT * (NW / 2) <= STG, "half the waves stage in each stage buffer");
@@ -463,6 +464,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
                                           silu_bf16out(g[4 * q + 1]) * u[4 * q + 1]);
                         h.y = pack_bf16x2(silu_bf16out(g[4 * q + 2]) * u[4 * q + 2],
                                           silu_bf16out(g[4 * q + 3]) * u[4 * q + 3]);
+                        *reinterpret_cast<u32x2_t*>(dst) = h;
+                    } else if (EPI == 2) {
+                        const f32x16_t& a = acc[i][j];
+                        u32x2_t h;
+                        h.x = pack_bf16x2(a[4 * q + 0], a[4 * q + 1]);
+                        h.y = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
                         *reinterpret_cast<u32x2_t*>(dst) = h;
                     } else {
                         const f32x16_t& a = acc[i][j];
@@ -581,7 +588,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     }
     t.Kdim = Kdim;
     t.N = N;
-    t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP ? 2 : 4);
+    t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP || EPI == 2 ? 2 : 4);
     const int nk_all = (Kdim + BK - 1) / BK;
     const int per_split = (nk_all + splits - 1) / splits;
     t.k_begin = min(nk_all, ks * per_split);
@@ -779,9 +786,9 @@ hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uin
     return hipGetLastError();
 }
 
-template <int NWV>
+template <int NWV, int EPI>
 hipError_t launch_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1, const uint16_t* B3,
-                       int b_split, const int32_t* offsets, int n, int Kdim, int N, float* C,
+                       int b_split, const int32_t* offsets, int n, int Kdim, int N, void* C,
                        int splits, hipStream_t s) {
     using SQ = Square<NWV>;
     const int64_t mslots = A_rows / SQ::BM + n;
@@ -789,25 +796,29 @@ hipError_t launch_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1, co
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int64_t stride = A_rows * (int64_t)N;
     if (Kdim % BK)
-        hipLaunchKernelGGL((gemm_bf16_kernel<false, true, NWV, 0, true>), dim3((unsigned)blocks),
-                           dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1, B3, offsets, n, Kdim,
-                           N, (void*)C, 8, splits, stride, b_split);
-    else
-        hipLaunchKernelGGL((gemm_bf16_kernel<false, false, NWV, 0, true>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, true, NWV, EPI, true>),
                            dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
-                           B3, offsets, n, Kdim, N, (void*)C, 8, splits, stride, b_split);
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, false, NWV, EPI, true>),
+                           dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
                                  const uint16_t* B3, int b_split, const int32_t* offsets, int n,
-                                 int Kdim, int N, float* C, int splits, hipStream_t s) {
+                                 int Kdim, int N, void* C, bool bf16_out, int splits,
+                                 hipStream_t s) {
     const int64_t lim = int64_t(1) << 31;
     if (N % 8 || Kdim % 8 || (B3 ? 2 * b_split != Kdim : b_split != Kdim) ||
-        A_rows * Kdim * 2 >= lim || (int64_t)b_split * N * 2 >= lim || splits < 1)
+        A_rows * Kdim * 2 >= lim || (int64_t)b_split * N * 2 >= lim || splits < 1 ||
+        (bf16_out && splits != 1))
         return hipErrorInvalidValue;
     // eight waves of 128 x 64 (measured 10% faster than four of 128 x 128 here)
-    return launch_krow<8>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, s);
+    if (bf16_out)
+        return launch_krow<8, 2>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, s);
+    return launch_krow<8, 0>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, s);
 }
 
 }  // namespace moe

@@ -42,13 +42,15 @@ hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uin
                                   int64_t b_stride, const int32_t* offsets, int n,
                                   int64_t A_rows, int N1, int N2, float* C, int GM,
                                   hipStream_t s);
-// C[s][p][c] (fp32, row stride N, split stride A_rows N) = sum over the K
-// range of split s of A[p][k] W_e[k][c], over the rows p of each expert e,
-// with K-row weights: W_e = B1 + e b_split N for k < b_split and
-// B3 + e b_split N (row k - b_split) beyond (B3 NULL: Kdim = b_split).
+// C[s][p][c] (row stride N, split stride A_rows N) = sum over the K range
+// of split s of A[p][k] W_e[k][c], over the rows p of each expert e, with
+// K-row weights: W_e = B1 + e b_split N for k < b_split and B3 + e b_split N
+// (row k - b_split) beyond (B3 NULL: Kdim = b_split).  C is fp32, or bf16
+// (rounded once) when bf16_out, which allows one split only.
 hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
                                  const uint16_t* B3, int b_split, const int32_t* offsets, int n,
-                                 int Kdim, int N, float* C, int splits, hipStream_t s);
+                                 int Kdim, int N, void* C, bool bf16_out, int splits,
+                                 hipStream_t s);
 // K splits worth using for the tiled down projection on `cus` compute units
 // (at most min(max_splits, 4)): the count that minimises tile rounds per split
 // plus the cost of the extra fp32 partial sums.  Depends on sizes only.
@@ -76,11 +78,11 @@ hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int 
                           const void* x, void* y, hipStream_t s);
 
 // ---- backward pass (backward.hip) ---------------------------------------------
-// Per assignment row p (a = perm[p]) from [a | b] = AB[p] and the fp32
+// Per assignment row p (a = perm[p]) from [a | b] = AB[p] and the bf16
 // gradient DH[p] of h with respect to the ungated expert output (W2_e^T dy):
 // dg[a] = h . DH[p] (h = bf16(SiLU(a) b)), DADB[p] = [da | db] of the gated
 // gradient gate[a] DH[p], GH[p] = bf16(gate[a] h).
-hipError_t launch_bwd_swiglu(const uint16_t* AB, const float* DH, const int32_t* perm,
+hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const int32_t* perm,
                              const float* gate, int64_t A, int dff, float* dg, uint16_t* DADB,
                              uint16_t* GH, hipStream_t s);
 // Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j sum_s
