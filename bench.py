@@ -214,15 +214,17 @@ def write_traffic(workload: str, dirs, command: str):
     print(json.dumps({workload: entry}), flush=True)
 
 
-def backward_cpu_baseline(w, L, dy, budget_s: float):
-    """The fp64 oracle's backward, as it stands, on the first tokens of the
-    workload (x and dy rows; all weight gradients of that sub-batch), repeated
-    until ~budget_s."""
+def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False):
+    """The fp64 oracle's backward (with train: its forward, then its backward),
+    as it stands, on the first tokens of the workload (x and dy rows; all
+    weight gradients of that sub-batch), repeated until ~budget_s."""
     import oracle
     H = {k: oracle._f32(v) for k, v in L.items()}
     dyh = oracle._f32(dy)
 
     def run(m):
+        if train:
+            oracle.forward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], w.K)
         oracle.backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K)
 
     t0 = time.perf_counter()
@@ -238,36 +240,50 @@ def backward_cpu_baseline(w, L, dy, budget_s: float):
         reps += 1
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"backward of the workload's first {m} tokens (x, dy rows; every "
-                      f"gradient) x{reps}",
+            "sample": f"{'forward and backward' if train else 'backward'} of the "
+                      f"workload's first {m} tokens (x, dy rows; every gradient) x{reps}",
             "seconds": round(elapsed, 2), "cpu": platform.processor() or platform.machine()}
 
 
-def bench_backward(args, w, dev):
+def bench_backward(args, w, dev, train=False):
     """One step = one moe_backward call: routing and the forward pieces
-    recomputed, dx and every weight gradient.  The dominant kernel is the
-    weight-gradient product (three launches per step, timed together)."""
+    recomputed, dx and every weight gradient; or, with train, one training
+    step: moe_forward_train (y and the saved state) then moe_backward_saved.
+    The dominant kernel is the weight-gradient product (three launches per
+    step, timed together)."""
     import torch
 
     import sparse_mixture_experts_14_amd as moe
     from sparse_mixture_experts_14_amd import workloads as W
     if w.name == "stack" or w.dtype != "bf16":
         raise SystemExit("--backward runs the single-layer bf16 workloads")
-    log(f"[bench] backward workload={w.name} T={w.T} building inputs on {dev}")
+    log(f"[bench] {'training step' if train else 'backward'} workload={w.name} T={w.T} "
+        f"building inputs on {dev}")
     L = W.make_layer(w, device=dev)
     g = torch.Generator(device=dev).manual_seed(w.seed + 7)
     dy = torch.randn(w.T, w.d, generator=g, device=dev).to(torch.bfloat16)
     ws = torch.empty(moe.backward_workspace_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
                      dtype=torch.uint8, device=dev)
     grads = moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws)
+    y = torch.empty_like(L["x"])
+    saved = torch.empty(moe.saved_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
+                        dtype=torch.uint8, device=dev)
+    fws = torch.empty(moe.workspace_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
             moe._lib.set_stage_events_raw("bwd_wgrad", ev[0].handle.value, ev[1].handle.value)
         else:
             moe._lib.set_stage_events_raw("bwd_wgrad")
-        moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
-                     out=grads)
+        if train:
+            moe.forward_train(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.K, out=y,
+                              saved=saved, workspace=fws)
+            moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
+                         out=grads, saved=saved)
+        else:
+            moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
+                         out=grads)
 
     for _ in range(args.warmup):
         step()
@@ -304,31 +320,36 @@ def bench_backward(args, w, dev):
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
     sha = kernel_source_sha(["gemm_bf16.hip", "common.hpp"])
-    roof["traffic"] = traffic_for(w.name + "-backward", sha)
-    roof["kernel"] = "weight-gradient product (MFMA tiles over 64-padded expert runs)"
+    kind = "train" if train else "backward"
+    roof["traffic"] = traffic_for(w.name + "-" + kind, sha)
+    roof["kernel"] = "weight-gradient product (MFMA tiles over each expert's rows)"
     roof["kernel_ms"] = round(k_avg, 5)
     roof["kernel_samples"] = len(k_ms)
     roof["algorithmic_bytes"] = wbytes
     roof["algorithmic_flops"] = flops
     roof["source_sha"] = sha
     out = {
-        "metric": "MoE-layer backward tokens/s (all gradients of sum(dy*y); top-2 of 8 "
-                  "SwiGLU, d=4096) + % roofline",
+        "metric": ("MoE-layer training-step tokens/s (forward keeping its routing and "
+                   "pre-activations, then all gradients of sum(dy*y)" if train else
+                   "MoE-layer backward tokens/s (all gradients of sum(dy*y)") +
+                  "; top-2 of 8 SwiGLU, d=4096) + % roofline",
         "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) tokens and output gradients, N(0,1/fan_in) "
                 "weights)",
-        "config": {"workload": w.name + "-backward", "T": w.T, "d": w.d, "d_ff": w.d_ff,
+        "config": {"workload": w.name + "-" + kind, "T": w.T, "d": w.d, "d_ff": w.d_ff,
                    "n": w.n, "K": w.K, "dtype": w.dtype},
         "roofline": roof,
-        # gate/up recompute 4, r = W2^T dy 2, dx 4, weight gradients 6 (x A d d_ff)
-        "step_tflops": round(16.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12, 1),
+        # backward: gate/up recompute 4, r = W2^T dy 2, dx 4, weight gradients
+        # 6; training step: forward 6 + backward without recompute 12 (x A d d_ff)
+        "step_tflops": round(18.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12 if train else
+                             16.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12, 1),
         "counts": counts,
     }
     if args.cpu_budget > 0:
         log("[bench] timing the fp64 oracle's backward on the host")
-        out["cpu_baseline"] = backward_cpu_baseline(w, L, dy, args.cpu_budget)
+        out["cpu_baseline"] = backward_cpu_baseline(w, L, dy, args.cpu_budget, train=train)
     print(json.dumps(out), flush=True)
 
 
@@ -354,6 +375,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward (all gradients of sum(dy * y)) instead of the "
                          "forward layer")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: moe_forward_train, then moe_backward_saved "
+                         "on its saved state")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(args.workload, args.traffic_from, args.traffic_command)
@@ -375,8 +399,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.load()
-    if args.backward:
-        bench_backward(args, w, dev)
+    if args.backward or args.train:
+        bench_backward(args, w, dev, train=args.train)
         return
     log(f"[bench] workload={w.name} T={w.T} building inputs on {dev}")
     if w.name == "stack":

@@ -170,7 +170,8 @@ size_t moe_backward_workspace_bytes(int64_t T, int64_t d, int64_t d_ff,
  * the products that consume them.  workspace: at least
  * moe_backward_workspace_bytes(...) bytes, 256-byte aligned.  dt = MOE_F32
  * returns MOE_ERR_UNSUPPORTED.  T = 0 zeroes the weight gradients (x, dy and
- * dx may then be NULL). */
+ * dx may then be NULL).  Weight gradients are cleared with kernels, never a
+ * memset, so the call can be captured into a HIP graph. */
 moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
                           const void* w3, const void* w2, const void* dy,
                           int64_t T, int64_t d, int64_t d_ff, int32_t n,
@@ -178,8 +179,38 @@ moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
                           float* dw1, float* dw3, float* dw2, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of the saved state that moe_forward_train writes and
+ * moe_backward_saved reads, for these sizes (bf16 only; 0 if invalid). */
+size_t moe_saved_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                       moe_dtype_t dt);
+
+/* moe_forward for training: the same y (bit for bit), and the routing, the
+ * per-expert permutation and the bf16 pre-activations [a | b] of every
+ * assignment kept in `saved` (caller-owned device memory of at least
+ * moe_saved_bytes(...) bytes, 256-byte aligned, opaque layout) for
+ * moe_backward_saved, which then need not recompute them.  bf16 plain layer
+ * only (MOE_ERR_UNSUPPORTED otherwise).  workspace as for moe_forward. */
+moe_status_t moe_forward_train(const void* x, const void* w_g, const void* w1,
+                               const void* w3, const void* w2, int64_t T, int64_t d,
+                               int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
+                               void* y, void* saved, size_t saved_bytes,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_backward from a saved state: `saved` must hold what moe_forward_train
+ * wrote for the same x, weights and sizes (the result is unspecified
+ * otherwise; it is not written).  The gradients equal moe_backward's bit for
+ * bit.  Workspace: moe_backward_workspace_bytes(...). */
+moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1,
+                                const void* w3, const void* w2, const void* dy,
+                                const void* saved, size_t saved_bytes, int64_t T,
+                                int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                                moe_dtype_t dt, void* dx, float* dw_g, float* dw1,
+                                float* dw3, float* dw2, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Timing hook (for profilers and benchmarks, not part of the layer): in later
- * moe_forward / moe_block_forward / moe_backward calls made by this thread, record
+ * moe_forward / moe_block_forward / moe_forward_train / moe_backward /
+ * moe_backward_saved calls made by this thread, record
  * start_event on the call's stream right before `stage` is launched and
  * end_event right after it.  Both are caller-owned hipEvent_t handles that
  * must stay valid while set; NULL, NULL clears the hook.  Returns

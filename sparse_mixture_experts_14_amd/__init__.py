@@ -9,9 +9,10 @@ stream; there is no CPU fallback.
 """
 from . import workloads  # noqa: F401  (seeded input generators; no layer arithmetic)
 from ._lib import (  # noqa: F401
-    Layer, MoeError, backward, backward_workspace_bytes, block_forward, forward, load, permute,
-    route, workspace_bytes,
+    Layer, MoeError, backward, backward_workspace_bytes, block_forward, forward, forward_train,
+    load, permute, route, saved_bytes, workspace_bytes,
 )
 
 __all__ = ["Layer", "MoeError", "backward", "backward_workspace_bytes", "block_forward",
-           "forward", "load", "permute", "route", "workspace_bytes", "workloads"]
+           "forward", "forward_train", "load", "permute", "route", "saved_bytes",
+           "workspace_bytes", "workloads"]

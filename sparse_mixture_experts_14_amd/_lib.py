@@ -25,7 +25,8 @@ MOE_BF16 = 1
 
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
-           "moe_last_error", "moe_backward", "moe_backward_workspace_bytes")
+           "moe_last_error", "moe_backward", "moe_backward_workspace_bytes",
+           "moe_saved_bytes", "moe_forward_train", "moe_backward_saved")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
           "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
@@ -75,6 +76,14 @@ def load(path: str | None = None):
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [V, V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, V, V,
                                  V, V, V, V, SZ, V]
+    lib.moe_saved_bytes.restype = SZ
+    lib.moe_saved_bytes.argtypes = [I64, I64, I64, I32, I32, ctypes.c_int]
+    lib.moe_forward_train.restype = ctypes.c_int
+    lib.moe_forward_train.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, V,
+                                      V, SZ, V, SZ, V]
+    lib.moe_backward_saved.restype = ctypes.c_int
+    lib.moe_backward_saved.argtypes = [V, V, V, V, V, V, V, SZ, I64, I64, I64, I32, I32,
+                                       ctypes.c_int, V, V, V, V, V, V, SZ, V]
     if path is None:
         _lib = lib
     return lib
@@ -224,12 +233,45 @@ def backward_workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int,
     return int(load().moe_backward_workspace_bytes(T, d, d_ff, n, K, code))
 
 
+def saved_bytes(T: int, d: int, d_ff: int, n: int, K: int, dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_saved_bytes(T, d, d_ff, n, K, code))
+
+
+def forward_train(x, Wg, W1, W3, W2, K: int, out=None, saved=None,
+                  workspace: torch.Tensor | None = None):
+    """y of the layer (bf16) plus the saved state for backward(..., saved=):
+    returns (y, saved) where saved is a uint8 device tensor."""
+    T, d = x.shape
+    n, d_ff, _ = W1.shape
+    nbytes = saved_bytes(T, d, d_ff, n, K, x.dtype)
+    if nbytes == 0:
+        raise ValueError("invalid sizes or dtype for forward_train (bf16 only)")
+    if saved is None:
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if saved.numel() < nbytes:
+        raise ValueError("saved buffer too small")
+    y = out if out is not None else torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(T, d, d_ff, n, K, x.dtype), 256),
+                                dtype=torch.uint8, device=x.device)
+    L = Layer.__new__(Layer)
+    L.T, L.d, L.d_ff, L.n, L.K, L.dtype = T, d, d_ff, n, K, x.dtype
+    px = L._args(x, Wg, W1, W3, W2)
+    st = load().moe_forward_train(*px, T, d, d_ff, n, K, _dtype_code(x), _dev(y, "y"),
+                                  saved.data_ptr(), saved.numel(), workspace.data_ptr(),
+                                  workspace.numel(), _stream(x.device))
+    _check(st, "moe_forward_train")
+    return y, saved
+
+
 def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None,
-             out: dict | None = None):
+             out: dict | None = None, saved: torch.Tensor | None = None):
     """Gradients of sum(dy * y) for bf16 inputs: a dict of dx (bf16 [T][d]) and
     dWg, dW1, dW3, dW2 (float32, in the layouts of W_g, W1, W3, W2).  ``out``
     (such a dict from an earlier call of the same sizes) is overwritten and
-    returned instead of new tensors."""
+    returned instead of new tensors.  ``saved`` (from forward_train on the same
+    inputs) replaces the recomputation of the routing and pre-activations."""
     T, d = x.shape
     n, d_ff, _ = W1.shape
     if Wg.shape != (d, n) or W1.shape != (n, d_ff, d) or W3.shape != (n, d_ff, d) \
@@ -256,10 +298,17 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = Non
         if out[k].dtype != dt or tuple(out[k].shape) != shp:
             raise ValueError(f"out[{k!r}] must be {dt} of shape {shp}")
     dx, dwg, dw1, dw3, dw2 = (out[k] for k in ("dx", "dWg", "dW1", "dW3", "dW2"))
-    st = load().moe_backward(_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"),
-                             _dev(W2, "W2"), _dev(dy, "dy"), T, d, d_ff, n, K, _dtype_code(x),
-                             _dev(dx, "dx"), _dev(dwg, "dW_g"), _dev(dw1, "dW1"),
-                             _dev(dw3, "dW3"), _dev(dw2, "dW2"), workspace.data_ptr(),
-                             workspace.numel(), _stream(dev))
-    _check(st, "moe_backward")
+    grads = (_dev(dx, "dx"), _dev(dwg, "dW_g"), _dev(dw1, "dW1"), _dev(dw3, "dW3"),
+             _dev(dw2, "dW2"))
+    ins = (_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"), _dev(W2, "W2"),
+           _dev(dy, "dy"))
+    if saved is not None:
+        st = load().moe_backward_saved(*ins, _dev(saved, "saved"), saved.numel(), T, d, d_ff,
+                                       n, K, _dtype_code(x), *grads, workspace.data_ptr(),
+                                       workspace.numel(), _stream(dev))
+        _check(st, "moe_backward_saved")
+    else:
+        st = load().moe_backward(*ins, T, d, d_ff, n, K, _dtype_code(x), *grads,
+                                 workspace.data_ptr(), workspace.numel(), _stream(dev))
+        _check(st, "moe_backward")
     return out

@@ -169,14 +169,64 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
+// ---- backward workspace and the saved training state ----------------------------
+// Workspace of moe_backward (bf16): routing and the pre-activation rows
+// [a | b] (recomputed), then the gradients in assignment (expert) order.
+// The saved state of moe_forward_train is exactly the first six regions
+// (idx .. AB), at the same offsets.
+struct BwdLayout {
+    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, total;
+};
+
+constexpr int kBwdMaxSplits = 4;  // K splits of the dx product
+
+BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
+    const size_t A = (size_t)T * (size_t)K;
+    const size_t dd = (size_t)d, ff = (size_t)d_ff;
+    BwdLayout L{};
+    size_t o = 0;
+    L.idx = o;     o = align256(o + A * 4);
+    L.gate = o;    o = align256(o + A * 4);
+    L.offsets = o; o = align256(o + (size_t)(n + 1) * 4);
+    L.perm = o;    o = align256(o + A * 4);
+    L.inv = o;     o = align256(o + A * 4);
+    L.AB = o;      o = align256(o + A * 2 * ff * 2);
+    L.DX = o;      o = align256(o + kBwdMaxSplits * A * dd * 4);
+    L.dg = o;      o = align256(o + A * 4);
+    L.DYG = o;     o = align256(o + A * dd * 2);
+    L.DH = o;      o = align256(o + A * ff * 2);
+    L.DADB = o;    o = align256(o + A * 2 * ff * 2);
+    L.GH = o;      o = align256(o + A * ff * 2);
+    L.XG = o;      o = align256(o + A * dd * 2);
+    L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
+    L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
+    L.total = o;
+    return L;
+}
+
+size_t saved_bytes_for(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
+    const BwdLayout L = bwd_layout(T, d, d_ff, n, K);
+    return L.AB + align256((size_t)T * (size_t)K * 2 * (size_t)d_ff * 2);
+}
+
 moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
                            const void* w3, const void* w2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, float eps,
                            void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
-                           float* gate_out, int32_t* counts_out, void* stream) {
-    const char* fn = block ? "moe_block_forward" : "moe_forward";
+                           float* gate_out, int32_t* counts_out, void* stream,
+                           void* saved = nullptr, size_t saved_bytes = 0) {
+    const char* fn = saved ? "moe_forward_train" : block ? "moe_block_forward" : "moe_forward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
+    if (saved) {
+        if (dt != MOE_BF16 || block)
+            return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 plain layer only", fn);
+        if (!aligned(saved, 256))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
+        if (saved_bytes < saved_bytes_for(T, d, d_ff, n, K))
+            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: saved %zu bytes < %zu needed", fn,
+                        saved_bytes, saved_bytes_for(T, d, d_ff, n, K));
+    }
     if (block && !(eps >= 0.0f && eps < 1e30f))
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
     const void* ptrs[] = {x, w_g, w1, w3, w2, y};
@@ -215,8 +265,15 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
         overlaps(y, ybytes, w1, wbytes) || overlaps(y, ybytes, w3, wbytes) ||
         overlaps(y, ybytes, w2, wbytes) || overlaps(y, ybytes, workspace, L.total) ||
         overlaps(y, ybytes, idx_out, A * 4) || overlaps(y, ybytes, gate_out, A * 4) ||
-        overlaps(y, ybytes, counts_out, (size_t)n * 4))
+        overlaps(y, ybytes, counts_out, (size_t)n * 4) || overlaps(y, ybytes, saved, saved_bytes))
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: y overlaps another argument", fn);
+    if (saved) {
+        const void* others[] = {x, w_g, w1, w3, w2, workspace};
+        const size_t osz[] = {ybytes, (size_t)d * n * es, wbytes, wbytes, wbytes, L.total};
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(saved, saved_bytes, others[i], osz[i]))
+                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved overlaps another argument", fn);
+    }
     if (T == 0) return MOE_OK;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -226,6 +283,17 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+    uint16_t* save_ab = nullptr;
+    if (saved) {  // the routing, the permutation and [a | b] go to the saved state
+        const BwdLayout SL = bwd_layout(T, d, d_ff, n, K);
+        char* sv = static_cast<char*>(saved);
+        idx = reinterpret_cast<int32_t*>(sv + SL.idx);
+        gate = reinterpret_cast<float*>(sv + SL.gate);
+        offsets = reinterpret_cast<int32_t*>(sv + SL.offsets);
+        perm = reinterpret_cast<int32_t*>(sv + SL.perm);
+        inv = reinterpret_cast<int32_t*>(sv + SL.inv);
+        save_ab = reinterpret_cast<uint16_t*>(sv + SL.AB);
+    }
     void* u = ws + L.u;
     void* H = ws + L.H;
     float* O = reinterpret_cast<float*>(ws + L.O);
@@ -281,7 +349,13 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                                    static_cast<const uint16_t*>(b3), offsets, n,
                                                    (int64_t)A, kdim, ndim, c_out,
                                                    gu ? 1 : splits,
-                                                   gu ? sk_gu.waves : sk_dn.waves, cus, s);
+                                                   gu ? sk_gu.waves : sk_dn.waves, cus, s,
+                                                   gu ? save_ab : nullptr);
+            else if (gu && save_ab)
+                err = moe::launch_gemm_bf16_gateup_save(
+                    static_cast<const uint16_t*>(a_in), T, pm, K,
+                    static_cast<const uint16_t*>(b1), static_cast<const uint16_t*>(b3), offsets,
+                    n, (int64_t)A, kdim, ndim, static_cast<uint16_t*>(c_out), save_ab, s);
             else
                 err = moe::launch_gemm_bf16_tiled(gu, static_cast<const uint16_t*>(a_in),
                                                   gu ? T : (int64_t)A, pm, K,
@@ -303,49 +377,23 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     return MOE_OK;
 }
 
-// ---- backward -------------------------------------------------------------------
-// Workspace of moe_backward (bf16): routing, recomputed forward pieces,
-// gradients in assignment (expert) order, transposed weights, and transposed,
-// expert-padded activations for the weight gradients.
-struct BwdLayout {
-    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, total;
-};
-
-constexpr int kBwdMaxSplits = 4;  // K splits of the dx product
-
-BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
-    const size_t A = (size_t)T * (size_t)K;
-    const size_t dd = (size_t)d, ff = (size_t)d_ff;
-    BwdLayout L{};
-    size_t o = 0;
-    L.idx = o;     o = align256(o + A * 4);
-    L.gate = o;    o = align256(o + A * 4);
-    L.offsets = o; o = align256(o + (size_t)(n + 1) * 4);
-    L.perm = o;    o = align256(o + A * 4);
-    L.inv = o;     o = align256(o + A * 4);
-    L.AB = o;      o = align256(o + A * 2 * ff * 2);
-    L.DX = o;      o = align256(o + kBwdMaxSplits * A * dd * 4);
-    L.dg = o;      o = align256(o + A * 4);
-    L.DYG = o;     o = align256(o + A * dd * 2);
-    L.DH = o;      o = align256(o + A * ff * 2);
-    L.DADB = o;    o = align256(o + A * 2 * ff * 2);
-    L.GH = o;      o = align256(o + A * ff * 2);
-    L.XG = o;      o = align256(o + A * dd * 2);
-    L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
-    L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
-    L.total = o;
-    return L;
-}
-
 moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, const void* w3,
                             const void* w2, const void* dy, int64_t T, int64_t d, int64_t d_ff,
                             int32_t n, int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
                             float* dw1, float* dw3, float* dw2, void* workspace,
-                            size_t ws_bytes, void* stream) {
-    const char* fn = "moe_backward";
+                            size_t ws_bytes, void* stream, const void* saved = nullptr,
+                            size_t saved_bytes = 0) {
+    const char* fn = saved ? "moe_backward_saved" : "moe_backward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
     if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+    if (saved) {
+        if (!aligned(saved, 256))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
+        if (saved_bytes < saved_bytes_for(T, d, d_ff, n, K))
+            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: saved %zu bytes < %zu needed", fn,
+                        saved_bytes, saved_bytes_for(T, d, d_ff, n, K));
+    }
     const void* ptrs[] = {x, w_g, w1, w3, w2, dy, dx, dw_g, dw1, dw3, dw2};
     const char* names[] = {"x", "w_g", "w1", "w3", "w2", "dy", "dx", "dw_g", "dw1", "dw3", "dw2"};
     for (int i = 0; i < 11; ++i) {
@@ -380,27 +428,32 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         for (int j = i + 1; j < 6; ++j)
             if (overlaps(outs[i], osz[i], outs[j], osz[j]))
                 return fail(MOE_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", fn);
+        if (overlaps(outs[i], osz[i], saved, saved_bytes))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: an output overlaps the saved state", fn);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     hipError_t err = hipSuccess;
-    if (T == 0) {  // no tokens: every weight gradient is zero
-        err = hipMemsetAsync(dw_g, 0, (size_t)d * n * 4, s);
-        if (err == hipSuccess) err = hipMemsetAsync(dw1, 0, wbytes * 4, s);
-        if (err == hipSuccess) err = hipMemsetAsync(dw3, 0, wbytes * 4, s);
-        if (err == hipSuccess) err = hipMemsetAsync(dw2, 0, wbytes * 4, s);
+    if (T == 0) {  // no tokens: every weight gradient is zero (fill kernels, no memset)
+        err = moe::launch_fill_zero(dw_g, (size_t)d * n * 4, s);
+        if (err == hipSuccess) err = moe::launch_fill_zero(dw1, wbytes * 4, s);
+        if (err == hipSuccess) err = moe::launch_fill_zero(dw3, wbytes * 4, s);
+        if (err == hipSuccess) err = moe::launch_fill_zero(dw2, wbytes * 4, s);
         if (err != hipSuccess) return hip_fail(err, "zero gradients");
         g_last_error[0] = '\0';
         return MOE_OK;
     }
     char* ws = static_cast<char*>(workspace);
+    // routing, permutation and [a | b]: from the saved state, else recomputed
+    // into the same regions of the workspace
+    char* rs = saved ? static_cast<char*>(const_cast<void*>(saved)) : ws;
     auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
-    int32_t* idx = static_cast<int32_t*>(at(L.idx));
-    float* gate = static_cast<float*>(at(L.gate));
-    int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
-    int32_t* perm = static_cast<int32_t*>(at(L.perm));
-    int32_t* inv = static_cast<int32_t*>(at(L.inv));
-    uint16_t* AB = static_cast<uint16_t*>(at(L.AB));
+    int32_t* idx = reinterpret_cast<int32_t*>(rs + L.idx);
+    float* gate = reinterpret_cast<float*>(rs + L.gate);
+    int32_t* offsets = reinterpret_cast<int32_t*>(rs + L.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(rs + L.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(rs + L.inv);
+    uint16_t* AB = reinterpret_cast<uint16_t*>(rs + L.AB);
     float* DX = static_cast<float*>(at(L.DX));
     float* dg = static_cast<float*>(at(L.dg));
     uint16_t* DYG = static_cast<uint16_t*>(at(L.DYG));
@@ -430,12 +483,25 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     const int cus = device_cus();
     // (the cost model's choice measured best: 4 splits at T = 4096)
     const int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
-    // routing and the pre-activations [a | b] recomputed
+    // routing and the pre-activations [a | b] recomputed, on the same kernels
+    // as the forward's (so a saved state from moe_forward_train is identical)
     if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
-    STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s), "router");
-    STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
-    STEP(moe::launch_gemm_bf16_gateup_ab(xb, T, perm, K, w1b, w3b, offsets, n, A, D, F, AB, s),
-         "gate/up recompute");
+    if (!saved) {
+        const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
+        STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s),
+             "router");
+        STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
+        if (plan.skinny) {
+            const SkinnyShape sk = choose_skinny(n, d_ff, d, 1, cus);
+            STEP(moe::launch_gemm_bf16_skinny(true, xb, T, perm, K, w1b, w3b, offsets, n, A, D,
+                                              F, nullptr, 1, sk.waves, cus, s, AB),
+                 "gate/up recompute");
+        } else {
+            STEP(moe::launch_gemm_bf16_gateup_ab(xb, T, perm, K, w1b, w3b, offsets, n, A, D, F,
+                                                 AB, s),
+                 "gate/up recompute");
+        }
+    }
     if (!mark(g_ev_end[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
     // tokens and output gradients of every assignment in expert order
@@ -571,6 +637,33 @@ size_t moe_backward_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t 
                                     moe_dtype_t dt) {
     if (check_sizes(T, d, d_ff, n, K, dt, true) != MOE_OK || dt != MOE_BF16) return 0;
     return bwd_layout(T, d, d_ff, n, K).total;
+}
+
+size_t moe_saved_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                       moe_dtype_t dt) {
+    if (check_sizes(T, d, d_ff, n, K, dt, true) != MOE_OK || dt != MOE_BF16) return 0;
+    return saved_bytes_for(T, d, d_ff, n, K);
+}
+
+moe_status_t moe_forward_train(const void* x, const void* w_g, const void* w1, const void* w3,
+                               const void* w2, int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                               int32_t K, moe_dtype_t dt, void* y, void* saved,
+                               size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!saved) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_forward_train: saved is NULL");
+    return layer_forward(false, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, 0.0f, y, workspace,
+                         workspace_bytes, nullptr, nullptr, nullptr, stream, saved, saved_bytes);
+}
+
+moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1, const void* w3,
+                                const void* w2, const void* dy, const void* saved,
+                                size_t saved_bytes, int64_t T, int64_t d, int64_t d_ff,
+                                int32_t n, int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
+                                float* dw1, float* dw3, float* dw2, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!saved) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_backward_saved: saved is NULL");
+    return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
+                          workspace, workspace_bytes, stream, saved, saved_bytes);
 }
 
 moe_status_t moe_backward(const void* x, const void* w_g, const void* w1, const void* w3,

@@ -209,6 +209,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     }
 }
 
+// Zero fill, 16 bytes per thread (a kernel, so that a captured graph never
+// holds a memset node); bytes is a multiple of 16.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, int64_t n16) {
+    for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < n16; q += (int64_t)gridDim.x * 256)
+        p[q] = uint4{0u, 0u, 0u, 0u};
+}
+
 unsigned grid_for(int64_t work, int64_t per_block) {
     const int64_t b = (work + per_block - 1) / per_block;
     return (unsigned)(b < 1 ? 1 : (b > 65535 * 16 ? 65535 * 16 : b));
@@ -257,6 +264,15 @@ hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, 
     const int64_t dn = (int64_t)d * n;
     hipLaunchKernelGGL(bwd_dwg_final_kernel, dim3(grid_for(dn, 256)), dim3(256), 0, s, part,
                        chunks, dn, dwg);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+    if (bytes % 16) return hipErrorInvalidValue;
+    if (bytes == 0) return hipSuccess;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, s,
+                       static_cast<uint4*>(p), n16);
     return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ struct TileArgs {
     const uint16_t* B3;
     int Kdim, N;
     void* Cout;           // already offset to this split's partial sums
+    void* Cout2 = nullptr;  // [a | b] rows (gate/up that stores H and [a | b])
     int row0, rows, n0;   // tile rows [row0, row0 + rows), first output column
     int k_begin, k_end;   // K steps of this split
     // K-row operands (stored [K][columns], the tile's M or N columns
@@ -111,6 +112,7 @@ __device__ __forceinline__ v4i16_t lds_read_tr(const uint8_t* p) {
 // LDS stages (separate objects, so the compiler can tell the stage being read
 // from the stage being filled).
 // EPI 2 (plain products): the fp32 sums are stored rounded to bf16.
+// EPI 3 (gate/up): H into Cout and the rows [a | b] into Cout2.
 // EPI (gate/up): 0 stores H = bf16(SiLU(a) * b); 1 stores the
 // pre-activations themselves, a and b in bf16, as rows [a | b] of 2 N columns
 // (the backward pass needs them).
@@ -437,12 +439,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     const int col_w = n0 + wn * OCOLS;  // first output column of this wave
     constexpr int CPR = OCOLS * ES / 16;      // 16-byte chunks per staged row
     constexpr int RPI = kWave / CPR;          // rows per store instruction
-    constexpr bool AB = GATEUP && EPI == 1;
-    const int64_t out_stride = AB ? 2 * (int64_t)N : N;
+    // Gate/up passes: EPI 0 stores H; EPI 1 stores a then b into rows
+    // [a | b] of t.Cout; EPI 3 stores H into t.Cout and then a, b into t.Cout2.
+    constexpr int PASSES = !GATEUP ? 1 : EPI == 1 ? 2 : EPI == 3 ? 3 : 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int half = 0; half < (AB ? 2 : 1); ++half) {
+        for (int pass = 0; pass < PASSES; ++pass) {
+            // pass writes H (h_pass) or the pre-activation half ab_half of [a | b]
+            const bool h_pass = GATEUP && (EPI == 0 || (EPI == 3 && pass == 0));
+            const int ab_half = EPI == 3 ? pass - 1 : pass;
             // stage rows wm*WTM + 32i .. +31
 #pragma unroll
             for (int j = 0; j < (GATEUP ? TN / 2 : TN); ++j) {
@@ -450,8 +456,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
                 for (int q = 0; q < 4; ++q) {
                     const int c = j * 32 + 8 * q + 4 * khalf;  // column within the wave
                     uint8_t* dst = slot + l32 * RSTRIDE + c * ES;
-                    if (AB) {
-                        const f32x16_t& v = acc[i][j + half * (TN / 2)];
+                    if (GATEUP && !h_pass) {
+                        const f32x16_t& v = acc[i][j + ab_half * (TN / 2)];
                         u32x2_t h;
                         h.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
                         h.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
@@ -489,8 +495,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
                 const u32x4_t v =
                     *reinterpret_cast<const u32x4_t*>(slot + r * RSTRIDE + ch * 16);
                 if (row < rows && col < N) {
-                    uint8_t* out = static_cast<uint8_t*>(t.Cout) +
-                                   ((int64_t)(t.row0 + row) * out_stride + half * N + col) * ES;
+                    uint8_t* out;
+                    if (GATEUP && !h_pass)  // [a | b] rows of 2 N columns
+                        out = static_cast<uint8_t*>(EPI == 3 ? t.Cout2 : t.Cout) +
+                              ((int64_t)(t.row0 + row) * 2 * N + ab_half * N + col) * ES;
+                    else
+                        out = static_cast<uint8_t*>(t.Cout) +
+                              ((int64_t)(t.row0 + row) * N + col) * ES;
                     *reinterpret_cast<u32x4_t*>(out) = v;
                 }
             }
@@ -506,7 +517,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
                       int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
-                      int64_t split_stride, int b_split = 0) {
+                      int64_t split_stride, int b_split = 0, void* __restrict__ Cout2 = nullptr) {
     // gate/up also runs wide tiles (larger stages)
     using SQ = Square<NWV>;
     using WD = Wide<NWV>;
@@ -589,6 +600,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     t.Kdim = Kdim;
     t.N = N;
     t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP || EPI == 2 ? 2 : 4);
+    t.Cout2 = Cout2;
     const int nk_all = (Kdim + BK - 1) / BK;
     const int per_split = (nk_all + splits - 1) / splits;
     t.k_begin = min(nk_all, ks * per_split);
@@ -611,7 +623,7 @@ template <bool GATEUP, int NWV = 4, int EPI = 0>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
-                        hipStream_t s) {
+                        hipStream_t s, void* C2 = nullptr) {
     using SQ = Square<NWV>;
     constexpr int BNO = GATEUP ? SQ::BN / 2 : SQ::BN;
     // upper bound of the tiles: each expert's last row tile may be partial
@@ -626,11 +638,11 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     if (ktail)
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride);
+                           N, C, GM, splits, stride, 0, C2);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride);
+                           N, C, GM, splits, stride, 0, C2);
     return hipGetLastError();
 }
 
@@ -753,6 +765,16 @@ hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, con
     if (!tiled_fits(A_src_rows, Kdim, N)) return hipErrorInvalidValue;
     return launch_tiled<true, 4, 1>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
                                     AB, 8, 1, s);
+}
+
+hipError_t launch_gemm_bf16_gateup_save(const uint16_t* A, int64_t A_src_rows,
+                                        const int32_t* perm, int K, const uint16_t* B1,
+                                        const uint16_t* B3, const int32_t* offsets, int n,
+                                        int64_t A_rows, int Kdim, int N, uint16_t* H,
+                                        uint16_t* AB, hipStream_t s) {
+    if (!tiled_fits(A_src_rows, Kdim, N) || !H || !AB) return hipErrorInvalidValue;
+    return launch_tiled<true, 4, 3>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
+                                    H, 8, 1, s, AB);
 }
 
 hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uint16_t* B,

@@ -132,12 +132,16 @@ constexpr int NT_AUX = 2;              // non-temporal cache policy
 // LDS position (in 16-byte units) of chunk q of tile row r.
 __device__ __forceinline__ int lds_pos(int r, int q) { return r * 64 + (q ^ r); }
 
-template <bool GATEUP, bool KTAIL, int WAVES>
+// SAVE (gate/up only): also store the pre-activation rows AB[p] = [a | b]
+// (bf16, 2 N columns); a NULL Cout then skips H (its stores fall out of a
+// zero-size range).
+template <bool GATEUP, bool KTAIL, int WAVES, bool SAVE = false>
 __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm, int K,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int32_t* __restrict__ offsets, int n, int Kdim, int N, void* __restrict__ Cout,
-    int64_t A_rows, int64_t A_src_rows, int nsplit, int ksplit) {
+    int64_t A_rows, int64_t A_src_rows, int nsplit, int ksplit,
+    uint16_t* __restrict__ AB = nullptr) {
     __shared__ Tables tb;
     __shared__ int s_touched;
     __shared__ u32x4_t tiles_lds[WAVES * TILE_U4];
@@ -181,7 +185,9 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
     const __amdgpu_buffer_rsrc_t a_rs = rsrc(A, (uint32_t)(A_src_rows * Kdim * 2));
     const uint32_t w_bytes = (uint32_t)N * row_bytes;  // one expert's matrix
     const uint32_t out_bytes = (uint32_t)((GATEUP ? 2 : 4) * (int64_t)nsplit * A_rows * N);
-    const __amdgpu_buffer_rsrc_t o_rs = rsrc(Cout, out_bytes);
+    const __amdgpu_buffer_rsrc_t o_rs = rsrc(Cout, Cout ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ab_rs =
+        rsrc(AB, SAVE ? (uint32_t)(2 * A_rows * (int64_t)N * 2) : 0u);
 
     // ---- weight rows: instruction i loads 1 KB of tile row i ------------------
     Cursor bc = start_cursor(tb, S, gw);  // position of the rows being loaded
@@ -259,6 +265,17 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
             h.y = pack_bf16x2(silu_bf16out(prev[2]) * acc[2], silu_bf16out(prev[3]) * acc[3]);
             const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + col) * 2) : OOB;
             __builtin_amdgcn_raw_buffer_store_b64(h, o_rs, off, 0, 0);
+            if (SAVE) {
+                u32x2_t va, vb;
+                va.x = pack_bf16x2(prev[0], prev[1]);
+                va.y = pack_bf16x2(prev[2], prev[3]);
+                vb.x = pack_bf16x2(acc[0], acc[1]);
+                vb.y = pack_bf16x2(acc[2], acc[3]);
+                const uint32_t oa = ok ? (uint32_t)(((int64_t)row * 2 * N + col) * 2) : OOB;
+                const uint32_t ob = ok ? oa + (uint32_t)N * 2u : OOB;
+                __builtin_amdgcn_raw_buffer_store_b64(va, ab_rs, oa, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(vb, ab_rs, ob, 0, 0);
+            }
         } else {
             const int64_t o = ((int64_t)w.split * A_rows + row) * N + col;
             const uint32_t off = ok ? (uint32_t)(o * 4) : OOB;
@@ -295,6 +312,8 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_skinny_kernel(
 }  // namespace
 
 bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits) {
+    // (the saved [a | b] rows of the gate/up are 2 A_rows N bf16 = the fp32
+    // partial sums of one split, covered below)
     // every buffer range must stay below 2^31 bytes (32-bit buffer offsets)
     const int64_t lim = int64_t(1) << 31;
     return A_rows <= MAX_ROWS && A_src_rows * Kdim * 2 < lim && N * Kdim * 2 < lim &&
@@ -305,26 +324,30 @@ hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src
                                    const int32_t* perm, int K, const uint16_t* B1,
                                    const uint16_t* B3, const int32_t* offsets, int n,
                                    int64_t A_rows, int Kdim, int N, void* C, int splits,
-                                   int waves, int cus, hipStream_t s) {
+                                   int waves, int cus, hipStream_t s, uint16_t* AB) {
     const int ksplit = (((Kdim + splits - 1) / splits) + 7) / 8 * 8;
     const int nsplit = (Kdim + ksplit - 1) / ksplit;
     if (!skinny_fits(A_src_rows, A_rows, Kdim, N, nsplit)) return hipErrorInvalidValue;
     if (waves != 7 && waves != 8) return hipErrorInvalidValue;
+    if (AB && !gateup) return hipErrorInvalidValue;
     const dim3 grid((unsigned)cus), block((unsigned)(waves * kWave));
     // every K split a whole number of steps: no partial chunks to zero
     const bool ktail = (ksplit % KSTEP) != 0 || (Kdim % ksplit) != 0;
-#define MOE_SKINNY(GU, KT, W)                                                               \
-    hipLaunchKernelGGL((gemm_skinny_kernel<GU, KT, W>), grid, block, 0, s, A, perm, K, B1, \
-                       B3, offsets, n, Kdim, N, C, A_rows, A_src_rows, nsplit, ksplit)
-#define MOE_SKINNY_W(GU, KT) \
-    if (waves == 7) MOE_SKINNY(GU, KT, 7); else MOE_SKINNY(GU, KT, 8)
+#define MOE_SKINNY(GU, KT, W, SV)                                                         \
+    hipLaunchKernelGGL((gemm_skinny_kernel<GU, KT, W, SV>), grid, block, 0, s, A, perm, K, \
+                       B1, B3, offsets, n, Kdim, N, C, A_rows, A_src_rows, nsplit, ksplit, AB)
+#define MOE_SKINNY_W(GU, KT, SV) \
+    if (waves == 7) MOE_SKINNY(GU, KT, 7, SV); else MOE_SKINNY(GU, KT, 8, SV)
+#define MOE_SKINNY_WS(GU, KT) \
+    if (AB) { MOE_SKINNY_W(GU, KT, true); } else { MOE_SKINNY_W(GU, KT, false); }
     if (gateup) {
-        if (ktail) { MOE_SKINNY_W(true, true); }
-        else { MOE_SKINNY_W(true, false); }
+        if (ktail) { MOE_SKINNY_WS(true, true); }
+        else { MOE_SKINNY_WS(true, false); }
     } else {
-        if (ktail) { MOE_SKINNY_W(false, true); }
-        else { MOE_SKINNY_W(false, false); }
+        if (ktail) { MOE_SKINNY_W(false, true, false); }
+        else { MOE_SKINNY_W(false, false, false); }
     }
+#undef MOE_SKINNY_WS
 #undef MOE_SKINNY_W
 #undef MOE_SKINNY
     return hipGetLastError();

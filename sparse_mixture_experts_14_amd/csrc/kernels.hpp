@@ -35,6 +35,13 @@ hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, con
                                       int K, const uint16_t* B1, const uint16_t* B3,
                                       const int32_t* offsets, int n, int64_t A_rows, int Kdim,
                                       int N, uint16_t* AB, hipStream_t s);
+// Gate/up grouped GEMM that stores both H (as launch_gemm_bf16_tiled) and the
+// pre-activation rows AB[p] = [a | b] (bf16, 2 N columns).
+hipError_t launch_gemm_bf16_gateup_save(const uint16_t* A, int64_t A_src_rows,
+                                        const int32_t* perm, int K, const uint16_t* B1,
+                                        const uint16_t* B3, const int32_t* offsets, int n,
+                                        int64_t A_rows, int Kdim, int N, uint16_t* H,
+                                        uint16_t* AB, hipStream_t s);
 // Per-expert weight gradients C_e[r][c] = sum over the expert's rows p of
 // A[p][r] B[p][c] (A, B bf16 in expert order, row strides a_stride,
 // b_stride); fp32 out, C_e = C + e N1 N2, zero for an expert without rows.
@@ -61,12 +68,14 @@ bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N);
 // bf16 MFMA grouped GEMMs streaming weights (few rows per expert), one
 // persistent workgroup of `waves` (7 or 8) waves per CU (`cus` of them).
 // The down projection may split K into partial sums; skinny_splits_used()
-// tells how many splits a request of `splits` really produces.
+// tells how many splits a request of `splits` really produces.  AB (gate/up
+// only, may be NULL): also store the pre-activation rows [a | b] (bf16, 2 N
+// columns); C may then be NULL to skip H.
 hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                    const int32_t* perm, int K, const uint16_t* B1,
                                    const uint16_t* B3, const int32_t* offsets, int n,
                                    int64_t A_rows, int Kdim, int N, void* C, int splits,
-                                   int waves, int cus, hipStream_t s);
+                                   int waves, int cus, hipStream_t s, uint16_t* AB = nullptr);
 // Whether the skinny kernels can take these sizes (row table in LDS, 32-bit
 // buffer offsets).
 bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits);
@@ -95,6 +104,8 @@ hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float*
 int bwd_dwg_chunks(int64_t T);
 hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, int n,
                           float* part, float* dwg, hipStream_t s);
+// Zero `bytes` (a multiple of 16) at p with a kernel.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // XG[p] = x[perm[p] / K] and YG[p] = y[perm[p] / K] (bf16 rows of d
 // elements), p < A.
 hipError_t launch_gather_rows(const uint16_t* x, const uint16_t* y, const int32_t* perm, int K,

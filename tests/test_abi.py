@@ -142,3 +142,50 @@ def test_binding_refuses_host_tensors():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         B.load(str(tmp_path / "missing.so"))
+
+
+def test_backward_and_training_state_validation(lib):
+    T, d, d_ff, n, K = 16, 64, 64, 8, 2
+    A = T * K
+    sb = lib.moe_saved_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    # routing arrays and the bf16 [a | b] rows
+    assert 4 * A * 4 + (n + 1) * 4 + A * 2 * d_ff * 2 <= sb < 4 * A * 4 + A * 4 * d_ff + 8192
+    assert lib.moe_saved_bytes(T, d, d_ff, n, K, B.MOE_F32) == 0
+    bw = lib.moe_backward_workspace_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    assert bw > sb and lib.moe_backward_workspace_bytes(T, d, d_ff, n, K, B.MOE_F32) == 0
+    ws, sv = FAKE * 256, FAKE * 1024
+
+    def fwd_train(**kw):
+        a = dict(x=FAKE, dt=B.MOE_BF16, y=FAKE * 64, saved=sv, saved_bytes=sb)
+        a.update(kw)
+        return lib.moe_forward_train(a["x"], FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d, d_ff,
+                                     n, K, a["dt"], a["y"], a["saved"], a["saved_bytes"], ws,
+                                     1 << 30, None)
+    assert fwd_train(saved=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert fwd_train(saved=sv + 16) == B.MOE_ERR_INVALID_ARGUMENT
+    assert fwd_train(saved_bytes=sb - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert fwd_train(dt=B.MOE_F32) == B.MOE_ERR_UNSUPPORTED
+    assert fwd_train(saved=ws) == B.MOE_ERR_INVALID_ARGUMENT  # overlaps the workspace
+    assert fwd_train(y=sv) == B.MOE_ERR_INVALID_ARGUMENT
+
+    def bwd(saved=None, saved_bytes=0, **kw):
+        a = dict(dx=FAKE * 64, dt=B.MOE_BF16, ws_bytes=bw, dwg=FAKE * 80)
+        a.update(kw)
+        args = (FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6)
+        grads = (a["dx"], a["dwg"], FAKE * 96, FAKE * 128, FAKE * 160, ws, a["ws_bytes"], None)
+        if saved is None:
+            return lib.moe_backward(*args, T, d, d_ff, n, K, a["dt"], *grads)
+        return lib.moe_backward_saved(*args, saved, saved_bytes, T, d, d_ff, n, K, a["dt"],
+                                      *grads)
+    assert bwd(dt=B.MOE_F32) == B.MOE_ERR_UNSUPPORTED
+    assert bwd(ws_bytes=bw - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(dx=FAKE + 8) == B.MOE_ERR_INVALID_ARGUMENT
+    assert bwd(dx=FAKE) == B.MOE_ERR_INVALID_ARGUMENT        # output overlaps x
+    assert bwd(dwg=FAKE * 64) == B.MOE_ERR_INVALID_ARGUMENT  # two outputs overlap
+    assert bwd(saved=sv + 16, saved_bytes=sb) == B.MOE_ERR_INVALID_ARGUMENT
+    assert bwd(saved=sv, saved_bytes=sb - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(saved=FAKE * 96, saved_bytes=sb) == B.MOE_ERR_INVALID_ARGUMENT  # overlaps dW1
+    assert lib.moe_backward_saved(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, None,
+                                  sb, T, d, d_ff, n, K, B.MOE_BF16, FAKE * 64, FAKE * 80,
+                                  FAKE * 96, FAKE * 128, FAKE * 160, ws, bw,
+                                  None) == B.MOE_ERR_INVALID_ARGUMENT

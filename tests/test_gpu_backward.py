@@ -71,6 +71,7 @@ def check_backward(L, K, dy, label, weights=True, rows=None):
     (77, 128, 192, 4, 4, 2),     # K = n: every expert on every token
     (45, 64, 96, 1, 1, 3),       # a single expert: the router gradient is zero
     (512, 512, 1024, 8, 2, 4),   # several tiles in every dimension of every product
+    (96, 128, 192, 64, 8, 6),    # the widest routing supported: n = 64, K = 8
 ])
 def test_backward_small(T, d, d_ff, n, K, seed):
     L = small_layer(T, d, d_ff, n, K, seed=seed)
