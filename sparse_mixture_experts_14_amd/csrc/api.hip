@@ -178,11 +178,47 @@ struct BwdLayout {
     size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, total;
 };
 
-constexpr int kBwdMaxSplits = 4;  // K splits of the dx product
+constexpr int kBwdMaxSplits = 4;  // K splits of the tiled dx product
+
+// K splits the weight-stream products may use for these sizes: partial sums
+// of at most 64 MiB per product, at most 32 splits.
+int stream_split_cap(int64_t A, int64_t d, int64_t d_ff) {
+    const int64_t row = A * (d > d_ff ? d : d_ff) * 4;
+    const int64_t cap = row > 0 ? (int64_t(64) << 20) / row : 32;
+    return (int)(cap < 1 ? 1 : cap > 32 ? 32 : cap);
+}
+
+// Waves per CU and K splits of a weight-stream K-row product over Kdim rows
+// and N columns: the pair whose items (all n experts touched, 512 columns
+// each) spread most evenly over the persistent waves; ties go to fewer
+// splits.
+SkinnyShape choose_stream(int32_t n, int64_t N, int64_t Kdim, int max_splits, int cus) {
+    const int64_t ncb = (N + 511) / 512;
+    SkinnyShape best{7, 1};
+    double best_eff = -1.0;
+    for (int s = 1; s <= max_splits; ++s) {
+        if (moe::krow_stream_splits_used((int)Kdim, s) != s) continue;
+        for (int w = 7; w <= 8; ++w) {
+            const int64_t items = (int64_t)n * ncb * s;
+            const int64_t nw = (int64_t)cus * w;
+            const int64_t rounds = (items + nw - 1) / nw;
+            const double eff = (double)items / (double)(rounds * nw);
+            if (eff > best_eff + 1e-9) {
+                best_eff = eff;
+                best = {w, s};
+            }
+        }
+    }
+    return best;
+}
 
 BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     const size_t A = (size_t)T * (size_t)K;
     const size_t dd = (size_t)d, ff = (size_t)d_ff;
+    // partial sums: the tiled dx product's, or the weight stream's (r, dx)
+    const size_t cap = (size_t)stream_split_cap((int64_t)A, d, d_ff);
+    const size_t dx_parts = cap > (size_t)kBwdMaxSplits ? cap : (size_t)kBwdMaxSplits;
+    const size_t dh_bytes = cap * A * ff * 4 > A * ff * 2 ? cap * A * ff * 4 : A * ff * 2;
     BwdLayout L{};
     size_t o = 0;
     L.idx = o;     o = align256(o + A * 4);
@@ -191,10 +227,10 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.perm = o;    o = align256(o + A * 4);
     L.inv = o;     o = align256(o + A * 4);
     L.AB = o;      o = align256(o + A * 2 * ff * 2);
-    L.DX = o;      o = align256(o + kBwdMaxSplits * A * dd * 4);
+    L.DX = o;      o = align256(o + dx_parts * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
     L.DYG = o;     o = align256(o + A * dd * 2);
-    L.DH = o;      o = align256(o + A * ff * 2);
+    L.DH = o;      o = align256(o + dh_bytes);
     L.DADB = o;    o = align256(o + A * 2 * ff * 2);
     L.GH = o;      o = align256(o + A * ff * 2);
     L.XG = o;      o = align256(o + A * dd * 2);
@@ -481,13 +517,22 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         return true;
     };
     const int cus = device_cus();
+    // the forward's GEMM family: MFMA tiles, or weight streams for few rows
+    // per expert
+    const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
     // (the cost model's choice measured best: 4 splits at T = 4096)
-    const int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
+    int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
+    SkinnyShape st_r{7, 1}, st_x{7, 1};
+    if (plan.skinny) {
+        const int cap = stream_split_cap(A, d, d_ff);
+        st_r = choose_stream(n, d_ff, d, cap, cus);
+        st_x = choose_stream(n, d, 2 * d_ff, cap, cus);
+        dx_splits = st_x.splits;
+    }
     // routing and the pre-activations [a | b] recomputed, on the same kernels
     // as the forward's (so a saved state from moe_forward_train is identical)
     if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     if (!saved) {
-        const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
         STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s),
              "router");
         STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
@@ -509,16 +554,33 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
          "row gather");
     // r = dy W2_e (W2_e [d][d_ff] read as K rows), then per row: dg = h . r,
     // [da | db] of g r, g h
-    STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, true, 1, s),
-         "dh product");
-    STEP(moe::launch_bwd_swiglu(AB, DH, perm, gate, A, F, dg, DADB, GH, s), "SwiGLU backward");
+    if (plan.skinny) {
+        float* DHP = reinterpret_cast<float*>(DH);
+        STEP(moe::launch_gemm_bf16_krow_stream(DYG, A, w2b, nullptr, D, offsets, n, D, F, DHP,
+                                               st_r.splits, st_r.waves, cus, s),
+             "dh product");
+        STEP(moe::launch_bwd_swiglu(AB, nullptr, DHP, st_r.splits, perm, gate, A, F, dg, DADB,
+                                    GH, s),
+             "SwiGLU backward");
+    } else {
+        STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, true, 1,
+                                        s),
+             "dh product");
+        STEP(moe::launch_bwd_swiglu(AB, DH, nullptr, 1, perm, gate, A, F, dg, DADB, GH, s),
+             "SwiGLU backward");
+    }
     if (!mark(g_ev_end[MOE_STAGE_BWD_DH])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
     // dx per assignment = da W1_e + db W3_e: K rows 0..d_ff-1 from W1_e, the
     // next d_ff from W3_e, against the rows [da | db]; K-split partials
-    STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, false,
-                                    dx_splits, s),
-         "dx product");
+    if (plan.skinny)
+        STEP(moe::launch_gemm_bf16_krow_stream(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX,
+                                               st_x.splits, st_x.waves, cus, s),
+             "dx product");
+    else
+        STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, false,
+                                        dx_splits, s),
+             "dx product");
     // router gradient, dx back in token order, dW_g
     STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, dx_splits,
                                A, inv, T, K, n, D, dl, static_cast<uint16_t*>(dx), s),

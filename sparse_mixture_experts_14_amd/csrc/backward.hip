@@ -29,8 +29,11 @@ __device__ __forceinline__ float bf(uint16_t v) { return bf16_bits_to_f32(v); }
 //   h = bf16(SiLU(a) b) (the forward's rounding point), dg[a] = sum h r
 //   (fixed-order block sum), dh = g r, da = dh b SiLU'(a), db = dh SiLU(a),
 //   DADB[p] = bf16([da | db]), GH[p] = bf16(g h).
+// PART: r arrives as S fp32 K-split partial sums (split stride sstride
+// elements), added in split order, instead of one bf16 row.
+template <bool PART>
 __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
-    const uint16_t* __restrict__ AB, const uint16_t* __restrict__ DH,
+    const uint16_t* __restrict__ AB, const void* __restrict__ DH, int S, int64_t sstride,
     const int32_t* __restrict__ perm, const float* __restrict__ gate, int dff,
     float* __restrict__ dg, uint16_t* __restrict__ DADB, uint16_t* __restrict__ GH) {
     __shared__ float part[4];
@@ -38,7 +41,8 @@ __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
     const int a_idx = perm[p];
     const float g = gate[a_idx];
     const uint16_t* ab = AB + p * 2 * dff;
-    const uint16_t* r = DH + p * dff;
+    const uint16_t* r = static_cast<const uint16_t*>(DH) + p * dff;
+    const float* rp = static_cast<const float*>(DH) + p * dff;
     uint16_t* dadb = DADB + p * 2 * dff;
     float acc = 0.0f;
     for (int c = threadIdx.x * 8; c < dff; c += 256 * 8) {
@@ -46,7 +50,18 @@ __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
         unpack_bf16x8(*reinterpret_cast<const uint4*>(ab + c), av);
         unpack_bf16x8(*reinterpret_cast<const uint4*>(ab + dff + c), bv);
         float rv[8];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(r + c), rv);
+        if (PART) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rv[i] = 0.0f;
+            for (int q = 0; q < S; ++q) {
+                const float4 r0 = *reinterpret_cast<const float4*>(rp + q * sstride + c);
+                const float4 r1 = *reinterpret_cast<const float4*>(rp + q * sstride + c + 4);
+                rv[0] += r0.x; rv[1] += r0.y; rv[2] += r0.z; rv[3] += r0.w;
+                rv[4] += r1.x; rv[5] += r1.y; rv[6] += r1.z; rv[7] += r1.w;
+            }
+        } else {
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(r + c), rv);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float sg = 1.0f / (1.0f + expf(-av[i]));
@@ -100,9 +115,10 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
             sdl[idx[t * K + j]] = gate[t * K + j] * (dg[t * K + j] - gdg);
     }
     __syncthreads();
-    if (threadIdx.x < n) dl[t * n + threadIdx.x] = sdl[threadIdx.x];
-    // four columns per thread: 16-byte loads of the partial sums
-    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+    if (threadIdx.x < n && blockIdx.y == 0) dl[t * n + threadIdx.x] = sdl[threadIdx.x];
+    // four columns per thread (16-byte loads of the partial sums); block y
+    // takes columns [1024 y, 1024 y + 1024) of every 1024 gridDim.y
+    for (int k = blockIdx.y * 1024 + threadIdx.x * 4; k < d; k += 1024 * gridDim.y) {
         float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int i = 0; i < n; ++i) {
 #pragma unroll
@@ -110,6 +126,7 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
         }
         for (int j = 0; j < K; ++j) {
             const float* src = DX + (int64_t)inv[t * K + j] * d + k;
+#pragma unroll 4
             for (int q = 0; q < S; ++q) {
                 const float4 v = *reinterpret_cast<const float4*>(src + q * split_stride);
                 s[0] += v.x;
@@ -223,12 +240,16 @@ unsigned grid_for(int64_t work, int64_t per_block) {
 
 }  // namespace
 
-hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const int32_t* perm,
-                             const float* gate, int64_t A, int dff, float* dg, uint16_t* DADB,
-                             uint16_t* GH, hipStream_t s) {
-    if (A > 0x7fffffff || dff % 8) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_swiglu_kernel, dim3((unsigned)A), dim3(256), 0, s, AB, DH, perm, gate,
-                       dff, dg, DADB, GH);
+hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float* DHP, int S,
+                             const int32_t* perm, const float* gate, int64_t A, int dff,
+                             float* dg, uint16_t* DADB, uint16_t* GH, hipStream_t s) {
+    if (A > 0x7fffffff || dff % 8 || (DHP && S < 1)) return hipErrorInvalidConfiguration;
+    if (DHP)
+        hipLaunchKernelGGL((bwd_swiglu_kernel<true>), dim3((unsigned)A), dim3(256), 0, s, AB,
+                           (const void*)DHP, S, A * dff, perm, gate, dff, dg, DADB, GH);
+    else
+        hipLaunchKernelGGL((bwd_swiglu_kernel<false>), dim3((unsigned)A), dim3(256), 0, s, AB,
+                           (const void*)DH, 1, (int64_t)0, perm, gate, dff, dg, DADB, GH);
     return hipGetLastError();
 }
 
@@ -237,8 +258,11 @@ hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float*
                             const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
                             uint16_t* dx, hipStream_t s) {
     if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)T), dim3(256), 0, s, wg, idx, gate, dg,
-                       DX, S, A * d, inv, K, n, d, dl, dx);
+    // few tokens: spread each token's columns over several blocks
+    const int ycols = (d + 1023) / 1024;
+    const int gy = T >= 1024 ? 1 : ycols;
+    hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)T, (unsigned)gy), dim3(256), 0, s, wg,
+                       idx, gate, dg, DX, S, A * d, inv, K, n, d, dl, dx);
     return hipGetLastError();
 }
 

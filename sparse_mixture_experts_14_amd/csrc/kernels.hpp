@@ -58,6 +58,16 @@ hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16
                                  const uint16_t* B3, int b_split, const int32_t* offsets, int n,
                                  int Kdim, int N, void* C, bool bf16_out, int splits,
                                  hipStream_t s);
+// Weight-stream variant of launch_gemm_bf16_krow for few rows per expert:
+// fp32 partial sums C[s][p][c] (split stride A_rows N) over `splits` K
+// ranges (krow_stream_splits_used() tells how many a request produces),
+// one persistent workgroup of `waves` (7 or 8) waves on each of `cus` CUs.
+int krow_stream_splits_used(int Kdim, int splits);
+hipError_t launch_gemm_bf16_krow_stream(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
+                                        const uint16_t* B3, int b_split,
+                                        const int32_t* offsets, int n, int Kdim, int N,
+                                        float* C, int splits, int waves, int cus,
+                                        hipStream_t s);
 // K splits worth using for the tiled down projection on `cus` compute units
 // (at most min(max_splits, 4)): the count that minimises tile rounds per split
 // plus the cost of the extra fp32 partial sums.  Depends on sizes only.
@@ -91,9 +101,11 @@ hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int 
 // gradient DH[p] of h with respect to the ungated expert output (W2_e^T dy):
 // dg[a] = h . DH[p] (h = bf16(SiLU(a) b)), DADB[p] = [da | db] of the gated
 // gradient gate[a] DH[p], GH[p] = bf16(gate[a] h).
-hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const int32_t* perm,
-                             const float* gate, int64_t A, int dff, float* dg, uint16_t* DADB,
-                             uint16_t* GH, hipStream_t s);
+// DHP (instead of DH, may be NULL): r as S fp32 K-split partial sums
+// [S][A][dff], added in split order.
+hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float* DHP, int S,
+                             const int32_t* perm, const float* gate, int64_t A, int dff,
+                             float* dg, uint16_t* DADB, uint16_t* GH, hipStream_t s);
 // Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j sum_s
 // DX[s][inv[t K + j]] (S K-split partials, split stride A d).
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,

@@ -156,3 +156,15 @@ def test_backward_prefill_size_sampled():
     for name, e in errs.items():
         assert e <= P.TOL_BF16, f"{name}: rel L2 {e} > {P.TOL_BF16}"
     assert scale > 0 and rs <= 1e-5 * scale * w.n
+
+
+@pytest.mark.parametrize("T,d,d_ff,n,K,seed,path", [
+    (40, 256, 328, 8, 2, 8, None),       # weight streams: ragged columns, a K chunk across W1 / W3
+    (200, 256, 328, 8, 2, 9, "skinny"),  # ~50 rows per expert: several 16-row passes
+    (96, 128, 192, 64, 8, 10, None),     # n = 64, K = 8 on the weight streams
+])
+def test_backward_weight_streams(T, d, d_ff, n, K, seed, path):
+    from tests.gpu_common import forced_path
+    L = small_layer(T, d, d_ff, n, K, seed=seed)
+    with forced_path(path):
+        check_backward(L, K, _dy(T, d, seed + 100), f"stream-{seed}")
