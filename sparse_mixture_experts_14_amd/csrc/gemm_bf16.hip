@@ -22,9 +22,9 @@
 // fragments from LDS for 16 MFMAs.  Down: eight waves of 128 x 64 (two per
 // SIMD, so a wave stalled on a load does not idle its SIMD's MFMA unit).  A
 // workgroup owns 256 token rows x 256 B rows (waves 2 x 2 or 2 x 4), or --
-// for an expert's last gate/up row tile when it has at most 128 rows -- 128
-// token rows x 512 B rows (waves 1 x 4), the same MFMA work over twice the
-// columns, so a short tail costs half a tile instead of a whole one.  Both
+// for an expert's last row tile when it has at most 128 rows -- 128 token
+// rows x 512 B rows (waves 1 x 4 or 1 x 8), the same MFMA work over twice
+// the columns, so a short tail costs half a tile instead of a whole one.  Both
 // operands are K-contiguous ([out][in] weights), the per-lane 8-element K
 // run each MFMA operand wants; the weights are the MFMA's first operand, so
 // a lane ends up owning 4 contiguous output columns.
@@ -517,11 +517,13 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const int32_t* __restrict__ perm, int K, const uint16_t* __restrict__ B1,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
                       int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
-                      int64_t split_stride, int b_split = 0, void* __restrict__ Cout2 = nullptr) {
-    // gate/up also runs wide tiles (larger stages)
+                      int64_t split_stride, int b_split = 0, void* __restrict__ Cout2 = nullptr,
+                      int down_wide_max = 0) {
+    // gate/up and the down projection may run wide tiles (larger stages)
     using SQ = Square<NWV>;
     using WD = Wide<NWV>;
-    constexpr int STG = GATEUP ? STAGE_MAX : SQ::STAGE_BYTES;
+    constexpr bool WIDE_OK = GATEUP || (!BKR && EPI == 0);
+    constexpr int STG = WIDE_OK ? STAGE_MAX : SQ::STAGE_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t S0[STG];
     __shared__ __attribute__((aligned(1024))) uint8_t S1[STG];
 
@@ -542,9 +544,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     constexpr int BNO_S = GATEUP ? SQ::BN / 2 : SQ::BN;  // output columns per tile
     const int ntn_s = (N + BNO_S - 1) / BNO_S;  // square column tiles
     const int npair = (ntn_s + 1) / 2;           // column pairs = wide column tiles
-    // Wide tail tiles pay off for gate/up; for the down projection (fewer,
-    // longer tiles) they measured slower, so its tails stay square.
-    constexpr int WIDE_MAX = GATEUP ? WD::BM : 0;
+    // Wide tail tiles: gate/up for every tail of at most 128 rows; the down
+    // projection for tails of at most down_wide_max rows.
+    const int WIDE_MAX = GATEUP ? WD::BM : WIDE_OK ? down_wide_max : 0;
     auto expert_tiles = [&](int m, int& nsq, int& nwide) {
         const int rem = m % SQ::BM;
         nsq = m / SQ::BM + (rem > WIDE_MAX ? 1 : 0);
@@ -611,7 +613,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         t.rows = min(SQ::BM, end - t.row0);
         t.n0 = (2 * c + L / gm) * BNO_S;
         tile_body<GATEUP, KTAIL, SQ, STG, EPI, false, BKR>(t, S0, S1);
-    } else if constexpr (WIDE_MAX > 0) {
+    } else if constexpr (WIDE_OK) {
         t.row0 = start + nsq * SQ::BM;
         t.rows = end - t.row0;
         t.n0 = 2 * c * BNO_S;
@@ -623,7 +625,7 @@ template <bool GATEUP, int NWV = 4, int EPI = 0>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
-                        hipStream_t s, void* C2 = nullptr) {
+                        hipStream_t s, void* C2 = nullptr, int down_wide_max = 0) {
     using SQ = Square<NWV>;
     constexpr int BNO = GATEUP ? SQ::BN / 2 : SQ::BN;
     // upper bound of the tiles: each expert's last row tile may be partial
@@ -638,11 +640,11 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     if (ktail)
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride, 0, C2);
+                           N, C, GM, splits, stride, 0, C2, down_wide_max);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride, 0, C2);
+                           N, C, GM, splits, stride, 0, C2, down_wide_max);
     return hipGetLastError();
 }
 
@@ -750,8 +752,10 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
     if (gateup)
         return launch_tiled<true, 4>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
                                      C, GM, 1, s);
+    // Down tails of at most 128 rows run wide as on gate/up (measured: 1%
+    // faster on the 32-layer stack at T = 2048, unchanged at T = 4096).
     return launch_tiled<false, 8>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
-                                  C, GM, splits, s);
+                                  C, GM, splits, s, nullptr, 128);
 }
 
 }  // namespace moe
