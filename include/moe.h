@@ -197,9 +197,10 @@ moe_status_t moe_forward_train(const void* x, const void* w_g, const void* w1,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_backward from a saved state: `saved` must hold what moe_forward_train
- * wrote for the same x, weights and sizes (the result is unspecified
- * otherwise; it is not written).  The gradients equal moe_backward's bit for
- * bit.  Workspace: moe_backward_workspace_bytes(...). */
+ * wrote for the same x, weights and sizes.  It is read, never written.  The
+ * gradients then equal moe_backward's bit for bit.  Any other contents are
+ * undefined behaviour: the kernels index rows with the saved permutation.
+ * Workspace: moe_backward_workspace_bytes(...). */
 moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1,
                                 const void* w3, const void* w2, const void* dy,
                                 const void* saved, size_t saved_bytes, int64_t T,
