@@ -144,6 +144,8 @@ def traffic_for(workload: str, src_sha: str):
 # Substrings naming the gate/up kernel in a rocprofv3 counter file, and the
 # plain copy kernel of the calibration run.
 GATE_UP_KERNEL = {"skinny": "gemm_skinny_kernel<true", "tiled": "gemm_bf16_kernel<true"}
+WGRAD_KERNEL = "gemm_wgrad_kernel"              # the backward's dominant kernel
+WGRAD_SOURCES = ["gemm_bf16.hip", "common.hpp"]
 COPY_KERNEL = "copy"
 COPY_BYTES = 512 << 20
 
@@ -182,20 +184,21 @@ def _counter_mean_kib(csv_path: str, counter: str, name_part: str) -> float:
     return sum(per[k] for k in ks) / len(ks)
 
 
-def write_traffic(workload: str, dirs, command: str):
-    """profiles/traffic.json[workload] from four rocprofv3 --pmc runs: the
-    bench's FETCH_SIZE and WRITE_SIZE, then the copy calibration's."""
+def write_traffic(workload: str, dirs, command: str, backward: bool = False):
+    """profiles/traffic.json[workload] (or [workload-backward], for the
+    weight-gradient product of the backward) from four rocprofv3 --pmc runs:
+    the bench's FETCH_SIZE and WRITE_SIZE, then the copy calibration's."""
     from sparse_mixture_experts_14_amd import workloads as W
     w = W.WORKLOADS[workload]
     skinny = w.dtype == "bf16" and w.T * w.K <= 16 * w.n
-    part = GATE_UP_KERNEL["skinny" if skinny else "tiled"]
+    part = WGRAD_KERNEL if backward else GATE_UP_KERNEL["skinny" if skinny else "tiled"]
     f_k, w_k, cf_k, cw_k = (os.path.join(d, "run_counter_collection.csv") for d in dirs)
     fetch = _counter_mean_kib(f_k, "FETCH_SIZE", part) * 1024
     write = _counter_mean_kib(w_k, "WRITE_SIZE", part) * 1024
     cfetch = _counter_mean_kib(cf_k, "FETCH_SIZE", COPY_KERNEL) * 1024
     cwrite = _counter_mean_kib(cw_k, "WRITE_SIZE", COPY_KERNEL) * 1024
     fs, ws = COPY_BYTES / cfetch, COPY_BYTES / cwrite
-    _, src = dominant_kernel(w, skinny)
+    src = WGRAD_SOURCES if backward else dominant_kernel(w, skinny)[1]
     entry = {"source_sha": kernel_source_sha(src), "kernel": part,
              "bytes_per_launch": round(fetch * fs + write * ws),
              "fetch_bytes_raw": round(fetch), "write_bytes_raw": round(write),
@@ -206,12 +209,13 @@ def write_traffic(workload: str, dirs, command: str):
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    data[workload] = entry
+    key = workload + "-backward" if backward else workload
+    data[key] = entry
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps({workload: entry}), flush=True)
+    print(json.dumps({key: entry}), flush=True)
 
 
 def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False):
@@ -319,9 +323,10 @@ def bench_backward(args, w, dev, train=False):
         ach = flops / (k_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-    sha = kernel_source_sha(["gemm_bf16.hip", "common.hpp"])
+    sha = kernel_source_sha(WGRAD_SOURCES)
     kind = "train" if train else "backward"
-    roof["traffic"] = traffic_for(w.name + "-" + kind, sha)
+    # the same kernel at the same sizes in both modes: one counter entry
+    roof["traffic"] = traffic_for(w.name + "-backward", sha)
     roof["kernel"] = "weight-gradient product (MFMA tiles over each expert's rows)"
     roof["kernel_ms"] = round(k_avg, 5)
     roof["kernel_samples"] = len(k_ms)
@@ -380,7 +385,8 @@ def main():
                          "on its saved state")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic(args.workload, args.traffic_from, args.traffic_command)
+        write_traffic(args.workload, args.traffic_from, args.traffic_command,
+                      backward=args.backward or args.train)
         return
     if args.copy_calibration:
         copy_calibration()
