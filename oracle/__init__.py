@@ -78,6 +78,12 @@ def _load():
     lib.oracle_backward_entries.restype = ctypes.c_int
     lib.oracle_backward_entries.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32, P,
                                             I64, P, P, P, P, P]
+    lib.oracle_block_backward.restype = ctypes.c_int
+    lib.oracle_block_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32, D,
+                                          P, I64, P, P, P, P, P, P]
+    lib.oracle_block_backward_entries.restype = ctypes.c_int
+    lib.oracle_block_backward_entries.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32,
+                                                  D, P, I64, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -201,6 +207,17 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, rows=None, forced=None, weights: boo
     """Gradients of L = sum_t dy_t . y_t (fp64).  Returns a dict with dx[R][d]
     (tokens ``rows``, all when None) and -- when ``weights`` and rows is None --
     dWg[d][n], dW1[n][d_ff][d], dW3[n][d_ff][d], dW2[n][d][d_ff]."""
+    return _backward(None, x, Wg, W1, W3, W2, dy, K, rows, forced, weights)
+
+
+def block_backward(x, Wg, W1, W3, W2, dy, K: int, eps: float, rows=None, forced=None,
+                   weights: bool = True):
+    """Gradients of L = sum_t dy_t . y_t for the stack layer
+    y = x + MoE(RMSNorm(x)) (fp64); same outputs as backward()."""
+    return _backward(float(eps), x, Wg, W1, W3, W2, dy, K, rows, forced, weights)
+
+
+def _backward(eps, x, Wg, W1, W3, W2, dy, K, rows, forced, weights):
     x = _f32(x)
     Wg = _f32(Wg)
     W1 = _f32(W1)
@@ -231,23 +248,28 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, rows=None, forced=None, weights: boo
         out["dW3"] = np.empty((n, d_ff, d), np.float64)
         out["dW2"] = np.empty((n, d, d_ff), np.float64)
     lib = _load()
-    rc = lib.oracle_backward(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dy), T, d,
-                             d_ff, n, K, _ptr(rows_a), R, _ptr(forced_a), _ptr(out["dx"]),
-                             _ptr(out.get("dWg")), _ptr(out.get("dW1")), _ptr(out.get("dW3")),
-                             _ptr(out.get("dW2")))
+    grads = (_ptr(out["dx"]), _ptr(out.get("dWg")), _ptr(out.get("dW1")),
+             _ptr(out.get("dW3")), _ptr(out.get("dW2")))
+    ins = (_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dy), T, d, d_ff, n, K)
+    if eps is None:
+        rc = lib.oracle_backward(*ins, _ptr(rows_a), R, _ptr(forced_a), *grads)
+    else:
+        rc = lib.oracle_block_backward(*ins, eps, _ptr(rows_a), R, _ptr(forced_a), *grads)
     if rc != 0:
-        raise ValueError(f"oracle_backward failed (rc={rc})")
+        raise ValueError(f"oracle backward failed (rc={rc})")
     return out
 
 
 _WHICH = {"dW1": 1, "dW2": 2, "dW3": 3}
 
 
-def backward_entries(x, Wg, W1, W3, W2, dy, K: int, entries, forced=None) -> np.ndarray:
+def backward_entries(x, Wg, W1, W3, W2, dy, K: int, entries, forced=None,
+                     eps: float | None = None) -> np.ndarray:
     """Selected expert weight-gradient entries (fp64), each summed over all the
     tokens routed to its expert.  ``entries``: sequence of (name, e, row, col)
     with name in dW1 / dW2 / dW3 and (row, col) indices of that matrix of
-    expert e.  ``forced`` ([T][K]) replaces TopK."""
+    expert e.  ``forced`` ([T][K]) replaces TopK.  ``eps``: the stack layer
+    (experts and router see RMSNorm(x))."""
     x = _f32(x)
     Wg = _f32(Wg)
     W1 = _f32(W1)
@@ -267,9 +289,13 @@ def backward_entries(x, Wg, W1, W3, W2, dy, K: int, entries, forced=None) -> np.
         forced_a = np.ascontiguousarray(np.asarray(forced, dtype=np.int32))
         assert forced_a.shape == (T, K)
     out = np.empty(max(Q, 1), np.float64)
-    rc = _load().oracle_backward_entries(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2),
-                                         _ptr(dy), T, d, d_ff, n, K, _ptr(forced_a), Q,
-                                         _ptr(which), _ptr(ex), _ptr(ri), _ptr(ci), _ptr(out))
+    lib = _load()
+    ins = (_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dy), T, d, d_ff, n, K)
+    sel = (_ptr(forced_a), Q, _ptr(which), _ptr(ex), _ptr(ri), _ptr(ci), _ptr(out))
+    if eps is None:
+        rc = lib.oracle_backward_entries(*ins, *sel)
+    else:
+        rc = lib.oracle_block_backward_entries(*ins, float(eps), *sel)
     if rc != 0:
         raise ValueError(f"oracle_backward_entries failed (rc={rc})")
     return out[:Q]

@@ -332,7 +332,7 @@ typedef struct {
     int32_t sel[64];
 } slot_grads;
 
-static void token_backward(const float* x, const float* Wg, const float* W1,
+static void token_backward(const double* x, const float* Wg, const float* W1,
                            const float* W3, const float* W2, const float* dy,
                            int64_t d, int64_t d_ff, int32_t n, int32_t K,
                            const int32_t* forced, double* dx, slot_grads* sg,
@@ -346,7 +346,7 @@ static void token_backward(const float* x, const float* Wg, const float* W1,
     int32_t* sel = sg->sel;
     for (int32_t i = 0; i < n; ++i) {
         double s = 0.0;
-        for (int64_t k = 0; k < d; ++k) s += (double)x[k] * (double)Wg[k * n + i];
+        for (int64_t k = 0; k < d; ++k) s += x[k] * (double)Wg[k * n + i];
         l[i] = s;
     }
     if (forced) {
@@ -365,8 +365,8 @@ static void token_backward(const float* x, const float* Wg, const float* W1,
         for (int64_t f = 0; f < d_ff; ++f) {
             double sa = 0.0, sb = 0.0;
             for (int64_t k = 0; k < d; ++k) {
-                sa += (double)w1[f * d + k] * (double)x[k];
-                sb += (double)w3[f * d + k] * (double)x[k];
+                sa += (double)w1[f * d + k] * x[k];
+                sb += (double)w3[f * d + k] * x[k];
             }
             a[f] = sa;
             b[f] = sb;
@@ -407,17 +407,14 @@ static void token_backward(const float* x, const float* Wg, const float* W1,
     }
 }
 
-/* Gradients of L = sum_t dy_t . y_t.  dy[T][d] is the output gradient;
- * forced (nullable, [R][K]) replaces TopK as in oracle_forward.  Outputs
- * (each nullable): dx[R][d] for the tokens in rows[0..R) (all T when rows is
- * NULL), and -- only when rows is NULL -- dWg[d][n], dW1[n][d_ff][d],
- * dW3[n][d_ff][d], dW2[n][d][d_ff], each summed over tokens in token order.
- * Returns 0, -1 on invalid arguments, -2 on allocation failure. */
-int oracle_backward(const float* x, const float* Wg, const float* W1, const float* W3,
-                    const float* W2, const float* dy, int64_t T, int64_t d, int64_t d_ff,
-                    int32_t n, int32_t K, const int64_t* rows, int64_t R,
-                    const int32_t* forced, double* dx, double* dWg, double* dW1,
-                    double* dW3, double* dW2) {
+/* The backward over input rows X[T][d] in fp64 (the layer's input, or its
+ * normalised input for a stack layer): dx below is the gradient with respect
+ * to X. */
+static int backward_impl(const double* x, const float* Wg, const float* W1, const float* W3,
+                         const float* W2, const float* dy, int64_t T, int64_t d, int64_t d_ff,
+                         int32_t n, int32_t K, const int64_t* rows, int64_t R,
+                         const int32_t* forced, double* dx, double* dWg, double* dW1,
+                         double* dW3, double* dW2) {
     if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n) return -1;
     const int weights = dWg || dW1 || dW3 || dW2;
     if (rows && weights) return -1;
@@ -481,7 +478,7 @@ int oracle_backward(const float* x, const float* Wg, const float* W1, const floa
             for (int32_t i = 0; i < n; ++i) {
                 double s = 0.0;
                 for (int64_t t = 0; t < T; ++t)
-                    s += (double)x[t * d + k] * SLOT(t, 0, K * per_slot)[i];
+                    s += x[t * d + k] * SLOT(t, 0, K * per_slot)[i];
                 dWg[k * n + i] = s;
             }
     }
@@ -494,7 +491,7 @@ int oracle_backward(const float* x, const float* Wg, const float* W1, const floa
                 for (int64_t t = 0; t < T; ++t)
                     for (int32_t j = 0; j < K; ++j)
                         if (keep_sel[t * K + j] == e) {
-                            const double xv = (double)x[t * d + k];
+                            const double xv = x[t * d + k];
                             s1 += SLOT(t, 0, j * d_ff)[f] * xv;
                             s3 += SLOT(t, 0, (size_t)K * d_ff + j * d_ff)[f] * xv;
                         }
@@ -524,6 +521,69 @@ int oracle_backward(const float* x, const float* Wg, const float* W1, const floa
     return 0;
 }
 
+/* Gradients of L = sum_t dy_t . y_t.  dy[T][d] is the output gradient;
+ * forced (nullable, [R][K]) replaces TopK as in oracle_forward.  Outputs
+ * (each nullable): dx[R][d] for the tokens in rows[0..R) (all T when rows is
+ * NULL), and -- only when rows is NULL -- dWg[d][n], dW1[n][d_ff][d],
+ * dW3[n][d_ff][d], dW2[n][d][d_ff], each summed over tokens in token order.
+ * Returns 0, -1 on invalid arguments, -2 on allocation failure. */
+int oracle_backward(const float* x, const float* Wg, const float* W1, const float* W3,
+                    const float* W2, const float* dy, int64_t T, int64_t d, int64_t d_ff,
+                    int32_t n, int32_t K, const int64_t* rows, int64_t R,
+                    const int32_t* forced, double* dx, double* dWg, double* dW1,
+                    double* dW3, double* dW2) {
+    if (T < 0 || d <= 0) return -1;
+    double* X = (double*)malloc(sizeof(double) * ((size_t)T * d + 1));
+    if (!X) return -2;
+    for (int64_t q = 0; q < T * d; ++q) X[q] = (double)x[q];
+    const int rc = backward_impl(X, Wg, W1, W3, W2, dy, T, d, d_ff, n, K, rows, R, forced, dx,
+                                 dWg, dW1, dW3, dW2);
+    free(X);
+    return rc;
+}
+
+/* Backward of a stack layer y = x + MoE(u), u = x / sqrt(mean(x^2) + eps)
+ * (unit weight; the layer of oracle_block_forward).  The MoE part is
+ * differentiated with respect to u (routing from u, as in the forward), then
+ * through the normalisation: with s = 1 / sqrt(mean(x^2) + eps),
+ *   du_k/dx_j = s (delta_kj - u_k u_j / d),
+ * so dx = dy + s (du - u (u . du) / d).  Same arguments and outputs as
+ * oracle_backward (weight gradients summed with u in place of x) plus eps. */
+int oracle_block_backward(const float* x, const float* Wg, const float* W1, const float* W3,
+                          const float* W2, const float* dy, int64_t T, int64_t d,
+                          int64_t d_ff, int32_t n, int32_t K, double eps, const int64_t* rows,
+                          int64_t R, const int32_t* forced, double* dx, double* dWg,
+                          double* dW1, double* dW3, double* dW2) {
+    if (T < 0 || d <= 0 || !(eps >= 0.0)) return -1;
+    if (!rows) R = T;
+    double* X = (double*)malloc(sizeof(double) * ((size_t)T * d + 1));
+    double* du = (double*)malloc(sizeof(double) * ((size_t)R * d + 1));
+    if (!X || !du) {
+        free(X);
+        free(du);
+        return -2;
+    }
+    for (int64_t t = 0; t < T; ++t) rms_normalize(x + t * d, d, eps, X + t * d);
+    int rc = backward_impl(X, Wg, W1, W3, W2, dy, T, d, d_ff, n, K, rows, R, forced,
+                           dx ? du : 0, dWg, dW1, dW3, dW2);
+    if (rc == 0 && dx) {
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t t = rows ? rows[r] : r;
+            const float* xt = x + t * d;
+            const double* u = X + t * d;
+            double ss = 0.0, c = 0.0;
+            for (int64_t k = 0; k < d; ++k) ss += (double)xt[k] * (double)xt[k];
+            const double sc = 1.0 / sqrt(ss / (double)d + eps);
+            for (int64_t k = 0; k < d; ++k) c += u[k] * du[r * d + k];
+            for (int64_t k = 0; k < d; ++k)
+                dx[r * d + k] = (double)dy[t * d + k] + sc * (du[r * d + k] - u[k] * c / (double)d);
+        }
+    }
+    free(X);
+    free(du);
+    return rc;
+}
+
 /* Selected entries of the expert weight gradients, for checks at sizes where
  * the full gradients are out of reach.  Each entry is summed over every token
  * routed to its expert, in token order, from the per-token definition above
@@ -537,12 +597,11 @@ int oracle_backward(const float* x, const float* Wg, const float* W1, const floa
  * and column ci[q] of that matrix.  Routing: forced[T][K] if given, else
  * TopK.  out[Q] in fp64.  Returns 0, -1 on invalid arguments, -2 on
  * allocation failure. */
-int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
-                            const float* W3, const float* W2, const float* dy, int64_t T,
-                            int64_t d, int64_t d_ff, int32_t n, int32_t K,
-                            const int32_t* forced, int64_t Q, const int32_t* which,
-                            const int32_t* ex, const int64_t* ri, const int64_t* ci,
-                            double* out) {
+static int entries_impl(const double* x, const float* Wg, const float* W1, const float* W3,
+                        const float* W2, const float* dy, int64_t T, int64_t d, int64_t d_ff,
+                        int32_t n, int32_t K, const int32_t* forced, int64_t Q,
+                        const int32_t* which, const int32_t* ex, const int64_t* ri,
+                        const int64_t* ci, double* out) {
     if (T < 0 || d <= 0 || d_ff <= 0 || n <= 0 || n > 64 || K <= 0 || K > n || Q < 0)
         return -1;
     for (int64_t q = 0; q < Q; ++q) {
@@ -565,7 +624,7 @@ int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
         for (int32_t i = 0; i < n; ++i) {
             double acc = 0.0;
             for (int64_t k = 0; k < d; ++k)
-                acc += (double)x[t * d + k] * (double)Wg[k * n + i];
+                acc += x[t * d + k] * (double)Wg[k * n + i];
             l[i] = acc;
         }
         if (forced) {
@@ -590,13 +649,13 @@ int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
         for (int64_t t = 0; t < T; ++t)
             for (int32_t j = 0; j < K; ++j) {
                 if (sel[t * K + j] != e) continue;
-                const float* xt = x + t * d;
+                const double* xt = x + t * d;
                 const float* dyt = dy + t * d;
                 const double g = gate[t * K + j];
                 double a = 0.0, b = 0.0;
                 for (int64_t k = 0; k < d; ++k) {
-                    a += (double)w1[k] * (double)xt[k];
-                    b += (double)w3[k] * (double)xt[k];
+                    a += (double)w1[k] * xt[k];
+                    b += (double)w3[k] * xt[k];
                 }
                 if (which[q] == 2) {
                     s += g * (double)dyt[ri[q]] * (silu(a) * b);
@@ -608,11 +667,45 @@ int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
                 const double sg = 1.0 / (1.0 + exp(-a));
                 const double unit = which[q] == 1 ? dh * b * (sg + a * sg * (1.0 - sg))
                                                   : dh * a * sg;
-                s += unit * (double)xt[ci[q]];
+                s += unit * xt[ci[q]];
             }
         out[q] = s;
     }
     free(sel);
     free(gate);
     return 0;
+}
+
+int oracle_backward_entries(const float* x, const float* Wg, const float* W1,
+                            const float* W3, const float* W2, const float* dy, int64_t T,
+                            int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                            const int32_t* forced, int64_t Q, const int32_t* which,
+                            const int32_t* ex, const int64_t* ri, const int64_t* ci,
+                            double* out) {
+    if (T < 0 || d <= 0) return -1;
+    double* X = (double*)malloc(sizeof(double) * ((size_t)T * d + 1));
+    if (!X) return -2;
+    for (int64_t q = 0; q < T * d; ++q) X[q] = (double)x[q];
+    const int rc = entries_impl(X, Wg, W1, W3, W2, dy, T, d, d_ff, n, K, forced, Q, which, ex,
+                                ri, ci, out);
+    free(X);
+    return rc;
+}
+
+/* The same entries for a stack layer: the experts' input is u = RMSNorm(x)
+ * (eps, unit weight) and the routing comes from u. */
+int oracle_block_backward_entries(const float* x, const float* Wg, const float* W1,
+                                  const float* W3, const float* W2, const float* dy, int64_t T,
+                                  int64_t d, int64_t d_ff, int32_t n, int32_t K, double eps,
+                                  const int32_t* forced, int64_t Q, const int32_t* which,
+                                  const int32_t* ex, const int64_t* ri, const int64_t* ci,
+                                  double* out) {
+    if (T < 0 || d <= 0 || !(eps >= 0.0)) return -1;
+    double* X = (double*)malloc(sizeof(double) * ((size_t)T * d + 1));
+    if (!X) return -2;
+    for (int64_t t = 0; t < T; ++t) rms_normalize(x + t * d, d, eps, X + t * d);
+    const int rc = entries_impl(X, Wg, W1, W3, W2, dy, T, d, d_ff, n, K, forced, Q, which, ex,
+                                ri, ci, out);
+    free(X);
+    return rc;
 }

@@ -183,3 +183,89 @@ def test_backward_entries_match_full_backward():
     _, idx, _, _ = oracle.forward(x, Wg, W1, W3, W2, 2)
     got_f = oracle.backward_entries(x, Wg, W1, W3, W2, dy, 2, ents, forced=idx)
     assert np.array_equal(got_f, got)
+
+
+# ---- the stack layer y = x + MoE(RMSNorm(x)) --------------------------------
+
+
+def _block_loss(x, Wg, W1, W3, W2, dy, K, eps):
+    y, idx, _, _ = oracle.block_forward(x, Wg, W1, W3, W2, K, eps)
+    return float(np.sum(y * dy.astype(np.float64))), idx
+
+
+def test_block_backward_matches_finite_differences():
+    rng = np.random.default_rng(21)
+    T, d, d_ff, n, K, eps = 3, 6, 5, 4, 2, 1e-2
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    g = oracle.block_backward(x, Wg, W1, W3, W2, dy, K, eps)
+    _, idx0 = _block_loss(x, Wg, W1, W3, W2, dy, K, eps)
+    h = 2.0 ** -9
+    for name, arr in {"dx": x, "dWg": Wg, "dW1": W1, "dW3": W3, "dW2": W2}.items():
+        flat = arr.reshape(-1)
+        num = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = np.float32(keep + h)
+            up = float(flat[i]) - float(keep)
+            lp, ip = _block_loss(x, Wg, W1, W3, W2, dy, K, eps)
+            flat[i] = np.float32(keep - h)
+            dn = float(keep) - float(flat[i])
+            lm, im = _block_loss(x, Wg, W1, W3, W2, dy, K, eps)
+            flat[i] = keep
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "routing moved"
+            num[i] = (lp - lm) / (up + dn)
+        np.testing.assert_allclose(g[name].reshape(-1), num, rtol=3e-5, atol=3e-6,
+                                   err_msg=name)
+
+
+def test_block_backward_dense_mixture_autograd():
+    # K = n: x + softmax-gated mixture of every expert on rms_norm(x), torch fp64
+    rng = np.random.default_rng(22)
+    T, d, d_ff, n, eps = 5, 8, 10, 4, 1e-5
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    g = oracle.block_backward(x, Wg, W1, W3, W2, dy, n, eps)
+    X = _t64(x).requires_grad_()
+    G = _t64(Wg).requires_grad_()
+    A1, A3, A2 = (_t64(w).requires_grad_() for w in (W1, W3, W2))
+    U = F.rms_norm(X, (d,), eps=eps)
+    gates = torch.softmax(U @ G, dim=1)
+    h = F.silu(torch.einsum("td,efd->tef", U, A1)) * torch.einsum("td,efd->tef", U, A3)
+    Y = X + (gates[:, :, None] * torch.einsum("tef,ecf->tec", h, A2)).sum(1)
+    (Y * _t64(dy)).sum().backward()
+    for name, ref in (("dx", X), ("dWg", G), ("dW1", A1), ("dW3", A3), ("dW2", A2)):
+        np.testing.assert_allclose(g[name], ref.grad.numpy(), rtol=1e-9, atol=1e-11,
+                                   err_msg=name)
+
+
+def test_block_backward_scale_invariance():
+    # eps = 0: RMSNorm(c x) = RMSNorm(x), so the weight gradients do not move,
+    # dx - dy scales by 1 / c, and x . (dx - dy) = 0 per token
+    rng = np.random.default_rng(23)
+    x, Wg, W1, W3, W2 = _layer(rng, 10, 12, 8, 8)
+    dy = rng.standard_normal((10, 12)).astype(np.float32)
+    g1 = oracle.block_backward(x, Wg, W1, W3, W2, dy, 2, 0.0)
+    g2 = oracle.block_backward(4.0 * x, Wg, W1, W3, W2, dy, 2, 0.0)  # exact in float32
+    for name in ("dWg", "dW1", "dW3", "dW2"):
+        np.testing.assert_allclose(g2[name], g1[name], rtol=1e-12, atol=1e-14, err_msg=name)
+    r1 = g1["dx"] - dy
+    np.testing.assert_allclose(g2["dx"] - dy, r1 / 4.0, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(np.sum(x.astype(np.float64) * r1, axis=1), 0.0, atol=1e-12)
+    assert np.abs(r1).max() > 1e-3
+
+
+def test_block_backward_entries_match_full_block_backward():
+    rng = np.random.default_rng(24)
+    T, d, d_ff, n, eps = 40, 16, 24, 8, 1e-5
+    x, Wg, W1, W3, W2 = _layer(rng, T, d, d_ff, n, scale_x=3.0)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    full = oracle.block_backward(x, Wg, W1, W3, W2, dy, 2, eps)
+    ents = _entries(rng, n, d, d_ff, 60)
+    got = oracle.backward_entries(x, Wg, W1, W3, W2, dy, 2, ents, eps=eps)
+    want = np.array([full[nm][e, i, j] for nm, e, i, j in ents])
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-13)
+    # rows= gives the same per-token dx
+    rows = np.array([5, 0, 39])
+    gr = oracle.block_backward(x, Wg, W1, W3, W2, dy, 2, eps, rows=rows)
+    assert np.array_equal(gr["dx"], full["dx"][rows])

@@ -67,7 +67,21 @@ BACKWARD_MUTANTS.update({
                               "r += (double)w2[f * d + c] * (double)dyt[c];"),
 })
 
+# Mistakes in the stack layer's backward (oracle_block_backward).
+BACKWARD_MUTANTS.update({
+    "block_projection_dropped": ("sc * (du[r * d + k] - u[k] * c / (double)d)",
+                                 "sc * du[r * d + k]"),
+    "block_residual_dropped": ("dx[r * d + k] = (double)dy[t * d + k] + sc",
+                               "dx[r * d + k] = 0.0 * (double)dy[t * d + k] + sc"),
+    "block_scale_missing": ("sc * (du[r * d + k] - u[k] * c / (double)d)",
+                            "(du[r * d + k] - u[k] * c / (double)d)"),
+})
+
 BACKWARD_PINS = [
+    lambda o: bpins.test_block_backward_matches_finite_differences(),
+    lambda o: bpins.test_block_backward_dense_mixture_autograd(),
+    lambda o: bpins.test_block_backward_scale_invariance(),
+    lambda o: bpins.test_block_backward_entries_match_full_block_backward(),
     lambda o: bpins.test_backward_entries_match_dense_autograd(),
     lambda o: bpins.test_backward_entries_match_full_backward(),
     lambda o: bpins.test_backward_matches_finite_differences(),
