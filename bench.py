@@ -218,10 +218,11 @@ def write_traffic(workload: str, dirs, command: str, backward: bool = False):
     print(json.dumps({key: entry}), flush=True)
 
 
-def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False):
-    """The fp64 oracle's backward (with train: its forward, then its backward),
-    as it stands, on the first tokens of the workload (x and dy rows; all
-    weight gradients of that sub-batch), repeated until ~budget_s."""
+def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False, eps=None):
+    """The fp64 oracle's backward (with train: its forward, then its backward;
+    with eps: the stack layer's), as it stands, on the first tokens of the
+    workload (x and dy rows; all weight gradients of that sub-batch),
+    repeated until ~budget_s."""
     import oracle
     H = {k: oracle._f32(v) for k, v in L.items()}
     dyh = oracle._f32(dy)
@@ -229,7 +230,11 @@ def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False):
     def run(m):
         if train:
             oracle.forward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], w.K)
-        oracle.backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K)
+        if eps is not None:
+            oracle.block_backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K,
+                                  eps)
+        else:
+            oracle.backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K)
 
     t0 = time.perf_counter()
     run(1)
@@ -259,16 +264,24 @@ def bench_backward(args, w, dev, train=False):
 
     import sparse_mixture_experts_14_amd as moe
     from sparse_mixture_experts_14_amd import workloads as W
-    if w.name == "stack" or w.dtype != "bf16":
-        raise SystemExit("--backward runs the single-layer bf16 workloads")
+    stack = w.name == "stack"
+    if w.dtype != "bf16" or (stack and train):
+        raise SystemExit("--backward runs the bf16 workloads (the stack: one layer's "
+                         "backward); --train the single-layer ones")
     log(f"[bench] {'training step' if train else 'backward'} workload={w.name} T={w.T} "
         f"building inputs on {dev}")
-    L = W.make_layer(w, device=dev)
+    if stack:  # the backward of layer 0 of the stack, on the stack's own input
+        L = dict(W.make_stack_layer(w, 0, device=dev))
+        L["x"] = W.make_stack_input(w, device=dev)
+    else:
+        L = W.make_layer(w, device=dev)
+    eps = w.eps if stack else None
     g = torch.Generator(device=dev).manual_seed(w.seed + 7)
     dy = torch.randn(w.T, w.d, generator=g, device=dev).to(torch.bfloat16)
     ws = torch.empty(moe.backward_workspace_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
                      dtype=torch.uint8, device=dev)
-    grads = moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws)
+    grads = moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
+                         eps=eps)
     y = torch.empty_like(L["x"])
     saved = torch.empty(moe.saved_bytes(w.T, w.d, w.d_ff, w.n, w.K, torch.bfloat16),
                         dtype=torch.uint8, device=dev)
@@ -287,7 +300,7 @@ def bench_backward(args, w, dev, train=False):
                          out=grads, saved=saved)
         else:
             moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
-                         out=grads)
+                         out=grads, eps=eps)
 
     for _ in range(args.warmup):
         step()
@@ -307,7 +320,10 @@ def bench_backward(args, w, dev, train=False):
     ms = start.elapsed_time(end) / args.steps
     k_ms = [a.elapsed_ms(b) / 3.0 for (a, b) in kev.values()]  # three launches per stage
     k_avg = sum(k_ms) / len(k_ms)
-    idx, _ = moe.route(L["x"], L["Wg"], w.K)
+    if stack:
+        _, idx, _, _ = moe.block_forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.K, eps)
+    else:
+        idx, _ = moe.route(L["x"], L["Wg"], w.K)
     counts = torch.bincount(idx.view(-1).long(), minlength=w.n).cpu().tolist()
     log(f"[bench] {ms:.4f} ms/step, weight-gradient product {k_avg:.4f} ms per launch")
     A = w.T * w.K
@@ -336,7 +352,8 @@ def bench_backward(args, w, dev, train=False):
     out = {
         "metric": ("MoE-layer training-step tokens/s (forward keeping its routing and "
                    "pre-activations, then all gradients of sum(dy*y)" if train else
-                   "MoE-layer backward tokens/s (all gradients of sum(dy*y)") +
+                   "MoE-layer backward tokens/s (all gradients of sum(dy*y)" +
+                   ("; the stack layer x + MoE(RMSNorm(x))" if stack else "")) +
                   "; top-2 of 8 SwiGLU, d=4096) + % roofline",
         "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -344,7 +361,8 @@ def bench_backward(args, w, dev, train=False):
         "data": "synthetic (seeded N(0,1) tokens and output gradients, N(0,1/fan_in) "
                 "weights)",
         "config": {"workload": w.name + "-" + kind, "T": w.T, "d": w.d, "d_ff": w.d_ff,
-                   "n": w.n, "K": w.K, "dtype": w.dtype},
+                   "n": w.n, "K": w.K, "dtype": w.dtype,
+                   **({"layers": 1, "layer": 0, "eps": eps} if stack else {})},
         "roofline": roof,
         # backward: gate/up recompute 4, r = W2^T dy 2, dx 4, weight gradients
         # 6; training step: forward 6 + backward without recompute 12 (x A d d_ff)
@@ -354,7 +372,8 @@ def bench_backward(args, w, dev, train=False):
     }
     if args.cpu_budget > 0:
         log("[bench] timing the fp64 oracle's backward on the host")
-        out["cpu_baseline"] = backward_cpu_baseline(w, L, dy, args.cpu_budget, train=train)
+        out["cpu_baseline"] = backward_cpu_baseline(w, L, dy, args.cpu_budget, train=train,
+                                                    eps=eps)
     print(json.dumps(out), flush=True)
 
 

@@ -179,6 +179,23 @@ moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
                           float* dw1, float* dw3, float* dw2, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Backward of the stack layer of moe_block_forward, y = x + MoE(u) with
+ * u = x / sqrt(mean(x^2) + eps): the gradients of sum_t dy_t . y_t.  The MoE
+ * part is differentiated as in moe_backward with u in place of x (the
+ * routing from the fp32 u, the experts on bf16(u)), then through the
+ * normalisation, plus the residual:
+ *   dx = dy + s (du - u (u . du) / d),  s = 1 / sqrt(mean(x^2) + eps),
+ * in fp32, rounded once.  dW_g sums the fp32 u.  Same arguments, layouts and
+ * workspace (moe_backward_workspace_bytes) as moe_backward, plus eps (>= 0).
+ * The normalisation and residual are this workload's definition, not the
+ * pages'. */
+moe_status_t moe_block_backward(const void* x, const void* w_g, const void* w1,
+                                const void* w3, const void* w2, const void* dy,
+                                int64_t T, int64_t d, int64_t d_ff, int32_t n,
+                                int32_t K, moe_dtype_t dt, float eps, void* dx,
+                                float* dw_g, float* dw1, float* dw3, float* dw2,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the saved state that moe_forward_train writes and
  * moe_backward_saved reads, for these sizes (bf16 only; 0 if invalid). */
 size_t moe_saved_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,

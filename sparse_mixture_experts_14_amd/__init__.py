@@ -9,10 +9,11 @@ stream; there is no CPU fallback.
 """
 from . import workloads  # noqa: F401  (seeded input generators; no layer arithmetic)
 from ._lib import (  # noqa: F401
-    Layer, MoeError, backward, backward_workspace_bytes, block_forward, forward, forward_train,
-    load, permute, route, saved_bytes, workspace_bytes,
+    Layer, MoeError, backward, backward_workspace_bytes, block_backward, block_forward, forward,
+    forward_train, load, permute, route, saved_bytes, workspace_bytes,
 )
 
-__all__ = ["Layer", "MoeError", "backward", "backward_workspace_bytes", "block_forward",
+__all__ = ["Layer", "MoeError", "backward", "backward_workspace_bytes", "block_backward",
+           "block_forward",
            "forward", "forward_train", "load", "permute", "route", "saved_bytes",
            "workspace_bytes", "workloads"]

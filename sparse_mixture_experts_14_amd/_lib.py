@@ -26,7 +26,8 @@ MOE_BF16 = 1
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
            "moe_last_error", "moe_backward", "moe_backward_workspace_bytes",
-           "moe_saved_bytes", "moe_forward_train", "moe_backward_saved")
+           "moe_saved_bytes", "moe_forward_train", "moe_backward_saved",
+           "moe_block_backward")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
           "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
@@ -84,6 +85,9 @@ def load(path: str | None = None):
     lib.moe_backward_saved.restype = ctypes.c_int
     lib.moe_backward_saved.argtypes = [V, V, V, V, V, V, V, SZ, I64, I64, I64, I32, I32,
                                        ctypes.c_int, V, V, V, V, V, V, SZ, V]
+    lib.moe_block_backward.restype = ctypes.c_int
+    lib.moe_block_backward.argtypes = [V, V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int,
+                                       F, V, V, V, V, V, V, SZ, V]
     if path is None:
         _lib = lib
     return lib
@@ -265,8 +269,16 @@ def forward_train(x, Wg, W1, W3, W2, K: int, out=None, saved=None,
     return y, saved
 
 
+def block_backward(x, Wg, W1, W3, W2, dy, K: int, eps: float,
+                   workspace: torch.Tensor | None = None, out: dict | None = None):
+    """Gradients of sum(dy * y) for the stack layer y = x + MoE(RMSNorm(x))
+    (bf16): the same dict as backward()."""
+    return backward(x, Wg, W1, W3, W2, dy, K, workspace=workspace, out=out, eps=eps)
+
+
 def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None,
-             out: dict | None = None, saved: torch.Tensor | None = None):
+             out: dict | None = None, saved: torch.Tensor | None = None,
+             eps: float | None = None):
     """Gradients of sum(dy * y) for bf16 inputs: a dict of dx (bf16 [T][d]) and
     dWg, dW1, dW3, dW2 (float32, in the layouts of W_g, W1, W3, W2).  ``out``
     (such a dict from an earlier call of the same sizes) is overwritten and
@@ -302,7 +314,14 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = Non
              _dev(dw2, "dW2"))
     ins = (_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"), _dev(W2, "W2"),
            _dev(dy, "dy"))
-    if saved is not None:
+    if eps is not None:
+        if saved is not None:
+            raise ValueError("the stack layer has no saved state")
+        st = load().moe_block_backward(*ins, T, d, d_ff, n, K, _dtype_code(x), float(eps),
+                                       *grads, workspace.data_ptr(), workspace.numel(),
+                                       _stream(dev))
+        _check(st, "moe_block_backward")
+    elif saved is not None:
         st = load().moe_backward_saved(*ins, _dev(saved, "saved"), saved.numel(), T, d, d_ff,
                                        n, K, _dtype_code(x), *grads, workspace.data_ptr(),
                                        workspace.numel(), _stream(dev))

@@ -175,7 +175,8 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // The saved state of moe_forward_train is exactly the first six regions
 // (idx .. AB), at the same offsets.
 struct BwdLayout {
-    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, total;
+    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, U, DU, SC,
+        total;
 };
 
 constexpr int kBwdMaxSplits = 4;  // K splits of the tiled dx product
@@ -236,6 +237,10 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.XG = o;      o = align256(o + A * dd * 2);
     L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
     L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
+    // stack layer: u = bf16(RMSNorm(x)), the gradient with respect to u, scales
+    L.U = o;       o = align256(o + (size_t)T * dd * 2);
+    L.DU = o;      o = align256(o + (size_t)T * dd * 4);
+    L.SC = o;      o = align256(o + (size_t)T * 4);
     L.total = o;
     return L;
 }
@@ -418,11 +423,15 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
                             int32_t n, int32_t K, moe_dtype_t dt, void* dx, float* dw_g,
                             float* dw1, float* dw3, float* dw2, void* workspace,
                             size_t ws_bytes, void* stream, const void* saved = nullptr,
-                            size_t saved_bytes = 0) {
-    const char* fn = saved ? "moe_backward_saved" : "moe_backward";
+                            size_t saved_bytes = 0, bool block = false, float eps = 0.0f) {
+    const char* fn = saved ? "moe_backward_saved" : block ? "moe_block_backward" : "moe_backward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
     if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+    if (block && !(eps >= 0.0f && eps < 1e30f))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    if (block && saved)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: no saved state for the stack layer", fn);
     if (saved) {
         if (!aligned(saved, 256))
             return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
@@ -499,7 +508,13 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     uint16_t* XG = static_cast<uint16_t*>(at(L.XG));
     float* dl = static_cast<float*>(at(L.dl));
     float* part = static_cast<float*>(at(L.part));
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint16_t* U = static_cast<uint16_t*>(at(L.U));
+    float* DU = static_cast<float*>(at(L.DU));
+    float* SC = static_cast<float*>(at(L.SC));
+    const uint16_t* x_in = static_cast<const uint16_t*>(x);
+    // the experts' input: x, or for the stack layer u = bf16(RMSNorm(x))
+    // (written by the router, which routes on the fp32 u)
+    const uint16_t* xb = block ? U : x_in;
     const uint16_t* w1b = static_cast<const uint16_t*>(w1);
     const uint16_t* w3b = static_cast<const uint16_t*>(w3);
     const uint16_t* w2b = static_cast<const uint16_t*>(w2);
@@ -533,7 +548,8 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     // as the forward's (so a saved state from moe_forward_train is identical)
     if (!mark(g_ev_start[MOE_STAGE_BWD_RECOMPUTE])) return hip_fail(err, "event record");
     if (!saved) {
-        STEP(moe::launch_router(true, false, x, w_g, T, D, n, K, 0.0f, idx, gate, nullptr, s),
+        STEP(moe::launch_router(true, block, x, w_g, T, D, n, K, eps, idx, gate,
+                                block ? U : nullptr, s),
              "router");
         STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
         if (plan.skinny) {
@@ -583,9 +599,17 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
              "dx product");
     // router gradient, dx back in token order, dW_g
     STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, dx_splits,
-                               A, inv, T, K, n, D, dl, static_cast<uint16_t*>(dx), s),
+                               A, inv, T, K, n, D, dl,
+                               block ? nullptr : static_cast<uint16_t*>(dx), block ? DU : nullptr,
+                               s),
          "token gradients");
-    STEP(moe::launch_bwd_dwg(xb, dl, T, D, n, part, dw_g, s), "router weight gradient");
+    if (block)  // through the normalisation, plus the residual
+        STEP(moe::launch_bwd_rms(x_in, static_cast<const uint16_t*>(dy), DU, T, D, eps,
+                                 static_cast<uint16_t*>(dx), SC, s),
+             "normalisation backward");
+    // dW_g = sum u dl^T with the router's own input: x, or the fp32 u = x s
+    STEP(moe::launch_bwd_dwg(x_in, block ? SC : nullptr, dl, T, D, n, part, dw_g, s),
+         "router weight gradient");
     if (!mark(g_ev_end[MOE_STAGE_BWD_DX])) return hip_fail(err, "event record");
     if (!mark(g_ev_start[MOE_STAGE_BWD_WGRAD])) return hip_fail(err, "event record");
     // weight gradients over each expert's rows: dW2_e = dy^T (g h),
@@ -726,6 +750,16 @@ moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1, 
     if (!saved) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_backward_saved: saved is NULL");
     return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
                           workspace, workspace_bytes, stream, saved, saved_bytes);
+}
+
+moe_status_t moe_block_backward(const void* x, const void* w_g, const void* w1,
+                                const void* w3, const void* w2, const void* dy, int64_t T,
+                                int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
+                                float eps, void* dx, float* dw_g, float* dw1, float* dw3,
+                                float* dw2, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
+                          workspace, workspace_bytes, stream, nullptr, 0, true, eps);
 }
 
 moe_status_t moe_backward(const void* x, const void* w_g, const void* w1, const void* w3,

@@ -98,12 +98,13 @@ __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
 
 // Per token: the router-logit gradient dl (thread 0, written to dl[t][n]),
 // then dx_t = W_g dl + sum_j sum_s DX[s][inv[t K + j]] in fp32 (in that
-// order), rounded once to bf16 (RNE).
+// order), rounded once to bf16 (RNE) -- or kept in fp32 (dx32, when given:
+// the gradient with respect to a stack layer's normalised input).
 __global__ __launch_bounds__(256) void bwd_token_kernel(
     const uint16_t* __restrict__ wg, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const float* __restrict__ dg, const float* __restrict__ DX,
     int S, int64_t split_stride, const int32_t* __restrict__ inv, int K, int n, int d,
-    float* __restrict__ dl, uint16_t* __restrict__ dx) {
+    float* __restrict__ dl, uint16_t* __restrict__ dx, float* __restrict__ dx32) {
     __shared__ float sdl[64];
     const int64_t t = blockIdx.x;
     if (threadIdx.x < 64) sdl[threadIdx.x] = 0.0f;
@@ -135,10 +136,74 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
                 s[3] += v.w;
             }
         }
-        uint2 o;
-        o.x = pack_bf16x2(s[0], s[1]);
-        o.y = pack_bf16x2(s[2], s[3]);
-        *reinterpret_cast<uint2*>(dx + t * d + k) = o;
+        if (dx32) {
+            *reinterpret_cast<float4*>(dx32 + t * d + k) = float4{s[0], s[1], s[2], s[3]};
+        } else {
+            uint2 o;
+            o.x = pack_bf16x2(s[0], s[1]);
+            o.y = pack_bf16x2(s[2], s[3]);
+            *reinterpret_cast<uint2*>(dx + t * d + k) = o;
+        }
+    }
+}
+
+// Stack layer y = x + MoE(u), u = x s, s = 1 / sqrt(mean(x^2) + eps): per
+// token, from the gradient du (fp32) with respect to u,
+//   dx = dy + s (du - u (u . du) / d)   (fp32, rounded once to bf16),
+// and the token's scale s for the router weight gradient.
+__global__ __launch_bounds__(256) void bwd_rms_kernel(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ dy,
+                                                      const float* __restrict__ du, int d,
+                                                      float eps, uint16_t* __restrict__ dx,
+                                                      float* __restrict__ scale) {
+    __shared__ float red[2][4];
+    const int64_t t = blockIdx.x;
+    const uint16_t* xt = x + t * d;
+    const float* dut = du + t * d;
+    float ss = 0.0f, xd = 0.0f;  // sum x^2, sum x du
+    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(xt + k);
+        const float4 g = *reinterpret_cast<const float4*>(dut + k);
+        const float a[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
+                            __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
+        ss = fmaf(a[0], a[0], ss);
+        ss = fmaf(a[1], a[1], ss);
+        ss = fmaf(a[2], a[2], ss);
+        ss = fmaf(a[3], a[3], ss);
+        xd = fmaf(a[0], g.x, xd);
+        xd = fmaf(a[1], g.y, xd);
+        xd = fmaf(a[2], g.z, xd);
+        xd = fmaf(a[3], g.w, xd);
+    }
+    ss = wave_sum(ss);
+    xd = wave_sum(xd);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        red[0][threadIdx.x / kWave] = ss;
+        red[1][threadIdx.x / kWave] = xd;
+    }
+    __syncthreads();
+    ss = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    xd = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const float sc = 1.0f / sqrtf(ss / (float)d + eps);
+    // u . du / d = s (x . du) / d
+    const float c = sc * xd / (float)d;
+    if (threadIdx.x == 0) scale[t] = sc;
+    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(xt + k);
+        const uint2 yv = *reinterpret_cast<const uint2*>(dy + t * d + k);
+        const float4 g = *reinterpret_cast<const float4*>(dut + k);
+        const float a[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
+                            __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
+        const float r[4] = {__uint_as_float(yv.x << 16), __uint_as_float(yv.x & 0xffff0000u),
+                            __uint_as_float(yv.y << 16), __uint_as_float(yv.y & 0xffff0000u)};
+        const float gv[4] = {g.x, g.y, g.z, g.w};
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = r[i] + sc * (gv[i] - (a[i] * sc) * c);
+        uint2 w;
+        w.x = pack_bf16x2(o[0], o[1]);
+        w.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(dx + t * d + k) = w;
     }
 }
 
@@ -147,8 +212,10 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
 // in token order.  The block's dl rows go through LDS 64 tokens at a time,
 // padded to NE columns with zeros, and each thread keeps 8 independent x
 // loads in flight.
+// scale (nullable): the rows are x[t] scale[t] (a stack layer's u).
 template <int NE>
 __global__ __launch_bounds__(256) void bwd_dwg_partial_kernel(const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ scale,
                                                              const float* __restrict__ dl,
                                                              int64_t T, int d, int n, int tpc,
                                                              float* __restrict__ part) {
@@ -166,7 +233,9 @@ __global__ __launch_bounds__(256) void bwd_dwg_partial_kernel(const uint16_t* __
         __syncthreads();
         for (int q = threadIdx.x; q < TB * NE; q += 256) {
             const int tt = q / NE, i = q % NE;
-            sdl[tt][i] = (tt < cnt && i < n) ? dl[(tb + tt) * n + i] : 0.0f;
+            sdl[tt][i] = (tt < cnt && i < n)
+                             ? dl[(tb + tt) * n + i] * (scale ? scale[tb + tt] : 1.0f)
+                             : 0.0f;
         }
         __syncthreads();
         if (k < d) {
@@ -256,34 +325,43 @@ hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,
                             const float* dg, const float* DX, int S, int64_t A,
                             const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
-                            uint16_t* dx, hipStream_t s) {
+                            uint16_t* dx, float* dx32, hipStream_t s) {
     if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
     // few tokens: spread each token's columns over several blocks
     const int ycols = (d + 1023) / 1024;
     const int gy = T >= 1024 ? 1 : ycols;
     hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)T, (unsigned)gy), dim3(256), 0, s, wg,
-                       idx, gate, dg, DX, S, A * d, inv, K, n, d, dl, dx);
+                       idx, gate, dg, DX, S, A * d, inv, K, n, d, dl, dx, dx32);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_rms(const uint16_t* x, const uint16_t* dy, const float* du, int64_t T,
+                          int d, float eps, uint16_t* dx, float* scale, hipStream_t s) {
+    if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_rms_kernel, dim3((unsigned)T), dim3(256), 0, s, x, dy, du, d, eps, dx,
+                       scale);
     return hipGetLastError();
 }
 
 int bwd_dwg_chunks(int64_t T) { return (int)((T + 63) / 64 < 256 ? (T + 63) / 64 : 256); }
 
-hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, int n,
-                          float* part, float* dwg, hipStream_t s) {
+hipError_t launch_bwd_dwg(const uint16_t* x, const float* scale, const float* dl, int64_t T,
+                          int d, int n, float* part, float* dwg, hipStream_t s) {
     const int chunks = bwd_dwg_chunks(T);
     const int tpc = (int)((T + chunks - 1) / chunks);
     const dim3 grid((unsigned)((d + 255) / 256), (unsigned)chunks);
     if (n <= 8)
-        hipLaunchKernelGGL((bwd_dwg_partial_kernel<8>), grid, dim3(256), 0, s, x, dl, T, d, n,
+        hipLaunchKernelGGL((bwd_dwg_partial_kernel<8>), grid, dim3(256), 0, s, x, scale, dl, T, d, n,
                            tpc, part);
     else if (n <= 16)
-        hipLaunchKernelGGL((bwd_dwg_partial_kernel<16>), grid, dim3(256), 0, s, x, dl, T, d, n,
+        hipLaunchKernelGGL((bwd_dwg_partial_kernel<16>), grid, dim3(256), 0, s, x, scale, dl, T, d, n,
                            tpc, part);
     else if (n <= 32)
-        hipLaunchKernelGGL((bwd_dwg_partial_kernel<32>), grid, dim3(256), 0, s, x, dl, T, d, n,
+        hipLaunchKernelGGL((bwd_dwg_partial_kernel<32>), grid, dim3(256), 0, s, x, scale, dl, T, d, n,
                            tpc, part);
     else
-        hipLaunchKernelGGL((bwd_dwg_partial_kernel<64>), grid, dim3(256), 0, s, x, dl, T, d, n,
+        hipLaunchKernelGGL((bwd_dwg_partial_kernel<64>), grid, dim3(256), 0, s, x, scale, dl, T, d, n,
                            tpc, part);
     const int64_t dn = (int64_t)d * n;
     hipLaunchKernelGGL(bwd_dwg_final_kernel, dim3(grid_for(dn, 256)), dim3(256), 0, s, part,

@@ -107,15 +107,21 @@ hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float
                              const int32_t* perm, const float* gate, int64_t A, int dff,
                              float* dg, uint16_t* DADB, uint16_t* GH, hipStream_t s);
 // Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j sum_s
-// DX[s][inv[t K + j]] (S K-split partials, split stride A d).
+// DX[s][inv[t K + j]] (S K-split partials, split stride A d): bf16 dx, or
+// fp32 dx32 when that is given.
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,
                             const float* dg, const float* DX, int S, int64_t A,
                             const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
-                            uint16_t* dx, hipStream_t s);
-// dW_g = sum_t x_t dl_t^T via fixed-order partial sums (part: chunks x d x n).
+                            uint16_t* dx, float* dx32, hipStream_t s);
+// Stack layer: dx = dy + s (du - u (u . du) / d) per token (u = x s,
+// s = 1 / sqrt(mean(x^2) + eps)); scale[t] = s.
+hipError_t launch_bwd_rms(const uint16_t* x, const uint16_t* dy, const float* du, int64_t T,
+                          int d, float eps, uint16_t* dx, float* scale, hipStream_t s);
+// dW_g = sum_t (x_t scale_t) dl_t^T (scale nullable: 1) via fixed-order
+// partial sums (part: chunks x d x n).
 int bwd_dwg_chunks(int64_t T);
-hipError_t launch_bwd_dwg(const uint16_t* x, const float* dl, int64_t T, int d, int n,
-                          float* part, float* dwg, hipStream_t s);
+hipError_t launch_bwd_dwg(const uint16_t* x, const float* scale, const float* dl, int64_t T,
+                          int d, int n, float* part, float* dwg, hipStream_t s);
 // Zero `bytes` (a multiple of 16) at p with a kernel.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // XG[p] = x[perm[p] / K] and YG[p] = y[perm[p] / K] (bf16 rows of d

@@ -168,3 +168,73 @@ def test_backward_weight_streams(T, d, d_ff, n, K, seed, path):
     L = small_layer(T, d, d_ff, n, K, seed=seed)
     with forced_path(path):
         check_backward(L, K, _dy(T, d, seed + 100), f"stream-{seed}")
+
+
+# ---- the stack layer y = x + MoE(RMSNorm(x)) --------------------------------
+
+EPS = 1e-5
+
+
+def check_block_backward(L, K, dy, label, rows=None, entries=None):
+    x = L["x"]
+    T, d = x.shape
+    n, d_ff, _ = L["W1"].shape
+    say(f"[case] block backward {label} T={T} d={d} d_ff={d_ff} n={n} K={K}")
+    got = moe.block_backward(x, L["Wg"], L["W1"], L["W3"], L["W2"], dy, K, EPS)
+    _, gi, gg, _ = moe.block_forward(x, L["Wg"], L["W1"], L["W3"], L["W2"], K, EPS)
+    torch.cuda.synchronize()
+    H = host_inputs(L)
+    gi, gg = P.to_np(gi), P.to_np(gg)
+    lg, oi, og = oracle.block_route(H["x"], H["Wg"], K, EPS)
+    rep = P.routing_report(gi, gg, lg, oi, og, K)
+    assert not rep["bad"], f"routing mismatch on tokens {rep['bad'][:10]}"
+    dyh = P.to_np(dy.float())
+    errs = {}
+    if rows is None:
+        ref = oracle.block_backward(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], dyh, K, EPS,
+                                    forced=gi)
+        for name in NAMES:
+            errs[name] = P.rel_l2(P.to_np(got[name].float()), ref[name])
+    else:
+        ref = oracle.block_backward(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], dyh, K, EPS,
+                                    rows=rows, forced=gi[rows])
+        errs["dx"] = P.rel_l2(P.to_np(got["dx"].float())[rows], ref["dx"])
+        want = oracle.backward_entries(H["x"], H["Wg"], H["W1"], H["W3"], H["W2"], dyh, K,
+                                       entries, forced=gi, eps=EPS)
+        have = np.array([got[nm][e, i, j].item() for nm, e, i, j in entries])
+        for name in ("dW1", "dW2", "dW3"):
+            sel = [q for q, en in enumerate(entries) if en[0] == name]
+            errs[name] = P.rel_l2(have[sel], want[sel])
+    rs = got["dWg"].double().sum(1).abs().max().item()
+    scale = got["dWg"].double().abs().max().item()
+    say("       " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
+        f" near_ties={rep['near_ties']} dWg_rowsum={rs:.1e}/{scale:.1e}")
+    for name, e in errs.items():
+        assert e <= P.TOL_BF16, f"{name}: rel L2 {e} > {P.TOL_BF16}"
+    assert scale > 0 and rs <= 1e-5 * scale * n
+
+
+@pytest.mark.parametrize("T,d,d_ff,n,K,seed", [
+    (300, 256, 328, 8, 2, 11),   # MFMA tiles
+    (40, 256, 328, 8, 2, 12),    # weight streams
+])
+def test_block_backward_small(T, d, d_ff, n, K, seed):
+    L = small_layer(T, d, d_ff, n, K, seed=seed)
+    check_block_backward(L, K, _dy(T, d, seed + 100), f"small-{seed}")
+
+
+def test_block_backward_stack_layer_sampled():
+    # layer 0 of the 32-layer stack workload (T = 2048, Mixtral widths, its own
+    # input and weights): sampled dx rows and weight-gradient entries
+    from sparse_mixture_experts_14_amd import workloads as W
+    w = W.WORKLOADS["stack"]
+    L = dict(W.make_stack_layer(w, 0, device="cuda"))
+    L["x"] = W.make_stack_input(w, device="cuda")
+    rng = np.random.default_rng(78)
+    rows = np.sort(rng.choice(w.T, 8, replace=False))
+    ents = []
+    for q in range(36):
+        name = ("dW1", "dW2", "dW3")[q % 3]
+        nr, nc = (w.d, w.d_ff) if name == "dW2" else (w.d_ff, w.d)
+        ents.append((name, q % w.n, int(rng.integers(nr)), int(rng.integers(nc))))
+    check_block_backward(L, w.K, _dy(w.T, w.d, 79), "stack-layer-0", rows=rows, entries=ents)
