@@ -228,7 +228,9 @@ def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False, eps=No
     dyh = oracle._f32(dy)
 
     def run(m):
-        if train:
+        if train and eps is not None:
+            oracle.block_forward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], w.K, eps)
+        elif train:
             oracle.forward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], w.K)
         if eps is not None:
             oracle.block_backward(H["x"][:m], H["Wg"], H["W1"], H["W3"], H["W2"], dyh[:m], w.K,
@@ -265,9 +267,9 @@ def bench_backward(args, w, dev, train=False):
     import sparse_mixture_experts_14_amd as moe
     from sparse_mixture_experts_14_amd import workloads as W
     stack = w.name == "stack"
-    if w.dtype != "bf16" or (stack and train):
-        raise SystemExit("--backward runs the bf16 workloads (the stack: one layer's "
-                         "backward); --train the single-layer ones")
+    if w.dtype != "bf16":
+        raise SystemExit("--backward and --train run the bf16 workloads (the stack: one "
+                         "layer)")
     log(f"[bench] {'training step' if train else 'backward'} workload={w.name} T={w.T} "
         f"building inputs on {dev}")
     if stack:  # the backward of layer 0 of the stack, on the stack's own input
@@ -295,9 +297,9 @@ def bench_backward(args, w, dev, train=False):
             moe._lib.set_stage_events_raw("bwd_wgrad")
         if train:
             moe.forward_train(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.K, out=y,
-                              saved=saved, workspace=fws)
+                              saved=saved, workspace=fws, eps=eps)
             moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
-                         out=grads, saved=saved)
+                         out=grads, saved=saved, eps=eps)
         else:
             moe.backward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], dy, w.K, workspace=ws,
                          out=grads, eps=eps)
@@ -352,8 +354,8 @@ def bench_backward(args, w, dev, train=False):
     out = {
         "metric": ("MoE-layer training-step tokens/s (forward keeping its routing and "
                    "pre-activations, then all gradients of sum(dy*y)" if train else
-                   "MoE-layer backward tokens/s (all gradients of sum(dy*y)" +
-                   ("; the stack layer x + MoE(RMSNorm(x))" if stack else "")) +
+                   "MoE-layer backward tokens/s (all gradients of sum(dy*y)") +
+                  ("; the stack layer x + MoE(RMSNorm(x))" if stack else "") +
                   "; top-2 of 8 SwiGLU, d=4096) + % roofline",
         "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

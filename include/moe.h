@@ -196,8 +196,9 @@ moe_status_t moe_block_backward(const void* x, const void* w_g, const void* w1,
                                 float* dw_g, float* dw1, float* dw3, float* dw2,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of the saved state that moe_forward_train writes and
- * moe_backward_saved reads, for these sizes (bf16 only; 0 if invalid). */
+/* Bytes of the saved state that moe_forward_train / moe_block_forward_train
+ * write and moe_backward_saved / moe_block_backward_saved read, for these
+ * sizes (bf16 only; 0 if invalid). */
 size_t moe_saved_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
                        moe_dtype_t dt);
 
@@ -225,6 +226,28 @@ moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1,
                                 moe_dtype_t dt, void* dx, float* dw_g, float* dw1,
                                 float* dw3, float* dw2, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* The training pair for the stack layer of moe_block_forward /
+ * moe_block_backward: the forward also keeps the routing, the permutation,
+ * [a | b] and the normalised input bf16(u) in `saved`
+ * (moe_saved_bytes(...) bytes, 256-byte aligned), and the backward uses them
+ * instead of recomputing.  y and the gradients equal moe_block_forward's and
+ * moe_block_backward's bit for bit.  The same rules for `saved` as for
+ * moe_backward_saved. */
+moe_status_t moe_block_forward_train(const void* x, const void* w_g, const void* w1,
+                                     const void* w3, const void* w2, int64_t T,
+                                     int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                                     moe_dtype_t dt, float eps, void* y, void* saved,
+                                     size_t saved_bytes, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+moe_status_t moe_block_backward_saved(const void* x, const void* w_g, const void* w1,
+                                      const void* w3, const void* w2, const void* dy,
+                                      const void* saved, size_t saved_bytes, int64_t T,
+                                      int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                                      moe_dtype_t dt, float eps, void* dx, float* dw_g,
+                                      float* dw1, float* dw3, float* dw2,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* Timing hook (for profilers and benchmarks, not part of the layer): in later
  * moe_forward / moe_block_forward / moe_forward_train / moe_backward /

@@ -27,7 +27,7 @@ EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
            "moe_last_error", "moe_backward", "moe_backward_workspace_bytes",
            "moe_saved_bytes", "moe_forward_train", "moe_backward_saved",
-           "moe_block_backward")
+           "moe_block_backward", "moe_block_forward_train", "moe_block_backward_saved")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
           "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
@@ -85,6 +85,12 @@ def load(path: str | None = None):
     lib.moe_backward_saved.restype = ctypes.c_int
     lib.moe_backward_saved.argtypes = [V, V, V, V, V, V, V, SZ, I64, I64, I64, I32, I32,
                                        ctypes.c_int, V, V, V, V, V, V, SZ, V]
+    lib.moe_block_forward_train.restype = ctypes.c_int
+    lib.moe_block_forward_train.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32,
+                                            ctypes.c_int, F, V, V, SZ, V, SZ, V]
+    lib.moe_block_backward_saved.restype = ctypes.c_int
+    lib.moe_block_backward_saved.argtypes = [V, V, V, V, V, V, V, SZ, I64, I64, I64, I32, I32,
+                                             ctypes.c_int, F, V, V, V, V, V, V, SZ, V]
     lib.moe_block_backward.restype = ctypes.c_int
     lib.moe_block_backward.argtypes = [V, V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int,
                                        F, V, V, V, V, V, V, SZ, V]
@@ -243,9 +249,10 @@ def saved_bytes(T: int, d: int, d_ff: int, n: int, K: int, dtype: torch.dtype) -
 
 
 def forward_train(x, Wg, W1, W3, W2, K: int, out=None, saved=None,
-                  workspace: torch.Tensor | None = None):
+                  workspace: torch.Tensor | None = None, eps: float | None = None):
     """y of the layer (bf16) plus the saved state for backward(..., saved=):
-    returns (y, saved) where saved is a uint8 device tensor."""
+    returns (y, saved) where saved is a uint8 device tensor.  ``eps``: the
+    stack layer y = x + MoE(RMSNorm(x)) (then backward needs the same eps)."""
     T, d = x.shape
     n, d_ff, _ = W1.shape
     nbytes = saved_bytes(T, d, d_ff, n, K, x.dtype)
@@ -262,18 +269,27 @@ def forward_train(x, Wg, W1, W3, W2, K: int, out=None, saved=None,
     L = Layer.__new__(Layer)
     L.T, L.d, L.d_ff, L.n, L.K, L.dtype = T, d, d_ff, n, K, x.dtype
     px = L._args(x, Wg, W1, W3, W2)
-    st = load().moe_forward_train(*px, T, d, d_ff, n, K, _dtype_code(x), _dev(y, "y"),
-                                  saved.data_ptr(), saved.numel(), workspace.data_ptr(),
-                                  workspace.numel(), _stream(x.device))
-    _check(st, "moe_forward_train")
+    if eps is None:
+        st = load().moe_forward_train(*px, T, d, d_ff, n, K, _dtype_code(x), _dev(y, "y"),
+                                      saved.data_ptr(), saved.numel(), workspace.data_ptr(),
+                                      workspace.numel(), _stream(x.device))
+        _check(st, "moe_forward_train")
+    else:
+        st = load().moe_block_forward_train(*px, T, d, d_ff, n, K, _dtype_code(x), float(eps),
+                                            _dev(y, "y"), saved.data_ptr(), saved.numel(),
+                                            workspace.data_ptr(), workspace.numel(),
+                                            _stream(x.device))
+        _check(st, "moe_block_forward_train")
     return y, saved
 
 
 def block_backward(x, Wg, W1, W3, W2, dy, K: int, eps: float,
-                   workspace: torch.Tensor | None = None, out: dict | None = None):
+                   workspace: torch.Tensor | None = None, out: dict | None = None,
+                   saved: torch.Tensor | None = None):
     """Gradients of sum(dy * y) for the stack layer y = x + MoE(RMSNorm(x))
     (bf16): the same dict as backward()."""
-    return backward(x, Wg, W1, W3, W2, dy, K, workspace=workspace, out=out, eps=eps)
+    return backward(x, Wg, W1, W3, W2, dy, K, workspace=workspace, out=out, saved=saved,
+                    eps=eps)
 
 
 def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = None,
@@ -314,9 +330,13 @@ def backward(x, Wg, W1, W3, W2, dy, K: int, workspace: torch.Tensor | None = Non
              _dev(dw2, "dW2"))
     ins = (_dev(x, "x"), _dev(Wg, "W_g"), _dev(W1, "W1"), _dev(W3, "W3"), _dev(W2, "W2"),
            _dev(dy, "dy"))
-    if eps is not None:
-        if saved is not None:
-            raise ValueError("the stack layer has no saved state")
+    if eps is not None and saved is not None:
+        st = load().moe_block_backward_saved(*ins, _dev(saved, "saved"), saved.numel(), T, d,
+                                             d_ff, n, K, _dtype_code(x), float(eps), *grads,
+                                             workspace.data_ptr(), workspace.numel(),
+                                             _stream(dev))
+        _check(st, "moe_block_backward_saved")
+    elif eps is not None:
         st = load().moe_block_backward(*ins, T, d, d_ff, n, K, _dtype_code(x), float(eps),
                                        *grads, workspace.data_ptr(), workspace.numel(),
                                        _stream(dev))

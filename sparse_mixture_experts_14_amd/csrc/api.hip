@@ -171,9 +171,10 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 // ---- backward workspace and the saved training state ----------------------------
 // Workspace of moe_backward (bf16): routing and the pre-activation rows
-// [a | b] (recomputed), then the gradients in assignment (expert) order.
-// The saved state of moe_forward_train is exactly the first six regions
-// (idx .. AB), at the same offsets.
+// [a | b] (recomputed), the stack layer's u, then the gradients in
+// assignment (expert) order.  The saved state of moe_forward_train /
+// moe_block_forward_train is exactly the first seven regions (idx .. U), at
+// the same offsets.
 struct BwdLayout {
     size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, U, DU, SC,
         total;
@@ -228,6 +229,8 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.perm = o;    o = align256(o + A * 4);
     L.inv = o;     o = align256(o + A * 4);
     L.AB = o;      o = align256(o + A * 2 * ff * 2);
+    // stack layer: u = bf16(RMSNorm(x)) (also part of the saved state)
+    L.U = o;       o = align256(o + (size_t)T * dd * 2);
     L.DX = o;      o = align256(o + dx_parts * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
     L.DYG = o;     o = align256(o + A * dd * 2);
@@ -237,8 +240,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.XG = o;      o = align256(o + A * dd * 2);
     L.dl = o;      o = align256(o + (size_t)T * (size_t)n * 4);
     L.part = o;    o = align256(o + (size_t)moe::bwd_dwg_chunks(T) * dd * (size_t)n * 4);
-    // stack layer: u = bf16(RMSNorm(x)), the gradient with respect to u, scales
-    L.U = o;       o = align256(o + (size_t)T * dd * 2);
+    // stack layer: the gradient with respect to u, the per-token scales
     L.DU = o;      o = align256(o + (size_t)T * dd * 4);
     L.SC = o;      o = align256(o + (size_t)T * 4);
     L.total = o;
@@ -247,7 +249,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
 
 size_t saved_bytes_for(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     const BwdLayout L = bwd_layout(T, d, d_ff, n, K);
-    return L.AB + align256((size_t)T * (size_t)K * 2 * (size_t)d_ff * 2);
+    return L.U + align256((size_t)T * (size_t)d * 2);
 }
 
 moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
@@ -256,12 +258,12 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                            void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
                            float* gate_out, int32_t* counts_out, void* stream,
                            void* saved = nullptr, size_t saved_bytes = 0) {
-    const char* fn = saved ? "moe_forward_train" : block ? "moe_block_forward" : "moe_forward";
+    const char* fn = saved ? (block ? "moe_block_forward_train" : "moe_forward_train")
+                           : block ? "moe_block_forward" : "moe_forward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
     if (saved) {
-        if (dt != MOE_BF16 || block)
-            return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 plain layer only", fn);
+        if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
         if (!aligned(saved, 256))
             return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
         if (saved_bytes < saved_bytes_for(T, d, d_ff, n, K))
@@ -324,6 +326,7 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+    void* u = ws + L.u;
     uint16_t* save_ab = nullptr;
     if (saved) {  // the routing, the permutation and [a | b] go to the saved state
         const BwdLayout SL = bwd_layout(T, d, d_ff, n, K);
@@ -334,8 +337,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
         perm = reinterpret_cast<int32_t*>(sv + SL.perm);
         inv = reinterpret_cast<int32_t*>(sv + SL.inv);
         save_ab = reinterpret_cast<uint16_t*>(sv + SL.AB);
+        if (block) u = sv + SL.U;  // the normalised input is saved too
     }
-    void* u = ws + L.u;
     void* H = ws + L.H;
     float* O = reinterpret_cast<float*>(ws + L.O);
     const bool bf16 = dt == MOE_BF16;
@@ -424,14 +427,14 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
                             float* dw1, float* dw3, float* dw2, void* workspace,
                             size_t ws_bytes, void* stream, const void* saved = nullptr,
                             size_t saved_bytes = 0, bool block = false, float eps = 0.0f) {
-    const char* fn = saved ? "moe_backward_saved" : block ? "moe_block_backward" : "moe_backward";
+    const char* fn = saved ? (block ? "moe_block_backward_saved" : "moe_backward_saved")
+                           : block ? "moe_block_backward" : "moe_backward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
     if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
     if (block && !(eps >= 0.0f && eps < 1e30f))
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
-    if (block && saved)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: no saved state for the stack layer", fn);
+
     if (saved) {
         if (!aligned(saved, 256))
             return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
@@ -508,7 +511,7 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     uint16_t* XG = static_cast<uint16_t*>(at(L.XG));
     float* dl = static_cast<float*>(at(L.dl));
     float* part = static_cast<float*>(at(L.part));
-    uint16_t* U = static_cast<uint16_t*>(at(L.U));
+    uint16_t* U = reinterpret_cast<uint16_t*>(rs + L.U);  // saved state or workspace
     float* DU = static_cast<float*>(at(L.DU));
     float* SC = static_cast<float*>(at(L.SC));
     const uint16_t* x_in = static_cast<const uint16_t*>(x);
@@ -750,6 +753,29 @@ moe_status_t moe_backward_saved(const void* x, const void* w_g, const void* w1, 
     if (!saved) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_backward_saved: saved is NULL");
     return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
                           workspace, workspace_bytes, stream, saved, saved_bytes);
+}
+
+moe_status_t moe_block_forward_train(const void* x, const void* w_g, const void* w1,
+                                     const void* w3, const void* w2, int64_t T, int64_t d,
+                                     int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
+                                     float eps, void* y, void* saved, size_t saved_bytes,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!saved) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_block_forward_train: saved is NULL");
+    return layer_forward(true, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, eps, y, workspace,
+                         workspace_bytes, nullptr, nullptr, nullptr, stream, saved, saved_bytes);
+}
+
+moe_status_t moe_block_backward_saved(const void* x, const void* w_g, const void* w1,
+                                      const void* w3, const void* w2, const void* dy,
+                                      const void* saved, size_t saved_bytes, int64_t T,
+                                      int64_t d, int64_t d_ff, int32_t n, int32_t K,
+                                      moe_dtype_t dt, float eps, void* dx, float* dw_g,
+                                      float* dw1, float* dw3, float* dw2, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (!saved)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_block_backward_saved: saved is NULL");
+    return layer_backward(x, w_g, w1, w3, w2, dy, T, d, d_ff, n, K, dt, dx, dw_g, dw1, dw3, dw2,
+                          workspace, workspace_bytes, stream, saved, saved_bytes, true, eps);
 }
 
 moe_status_t moe_block_backward(const void* x, const void* w_g, const void* w1,

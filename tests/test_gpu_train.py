@@ -60,3 +60,27 @@ def test_training_pair_no_tokens():
     assert y.shape == (0, 64)
     for name in ("dWg", "dW1", "dW3", "dW2"):
         assert not torch.any(g[name]), name
+
+
+@pytest.mark.parametrize("T,d,d_ff,n,K,path,seed", [
+    (48, 256, 320, 8, 2, None, 11),       # weight stream
+    (300, 256, 328, 8, 2, None, 12),      # tiles
+    (77, 128, 192, 4, 4, "tiled", 13),
+])
+def test_block_training_pair(T, d, d_ff, n, K, path, seed):
+    # the stack layer y = x + MoE(RMSNorm(x)): forward_train's y equals
+    # block_forward's, the saved-state backward equals block_backward
+    eps = 1e-5
+    L = small_layer(T, d, d_ff, n, K, seed=seed)
+    dy = _dy(T, d, seed + 50)
+    say(f"[case] block training pair T={T} d={d} d_ff={d_ff} n={n} K={K} path={path}")
+    args = (L["x"], L["Wg"], L["W1"], L["W3"], L["W2"])
+    with forced_path(path):
+        y_ref, _, _, _ = moe.block_forward(*args, K, eps)
+        y, saved = moe.forward_train(*args, K, eps=eps)
+        g_ref = moe.block_backward(*args, dy, K, eps)
+        g = moe.block_backward(*args, dy, K, eps, saved=saved)
+        torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "block forward_train y differs from block_forward"
+    for name in NAMES:
+        assert torch.equal(g[name], g_ref[name]), f"{name} from the saved state differs"
