@@ -189,3 +189,27 @@ def test_backward_and_training_state_validation(lib):
                                   sb, T, d, d_ff, n, K, B.MOE_BF16, FAKE * 64, FAKE * 80,
                                   FAKE * 96, FAKE * 128, FAKE * 160, ws, bw,
                                   None) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_block_backward_and_training_pair_validation(lib):
+    T, d, d_ff, n, K = 16, 64, 64, 8, 2
+    sb = lib.moe_saved_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    bw = lib.moe_backward_workspace_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    ws, sv = FAKE * 256, FAKE * 1024
+    ins = (FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6)
+    grads = (FAKE * 64, FAKE * 80, FAKE * 96, FAKE * 128, FAKE * 160, ws, bw, None)
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert lib.moe_block_backward(*ins, T, d, d_ff, n, K, B.MOE_BF16, eps,
+                                      *grads) == B.MOE_ERR_INVALID_ARGUMENT
+        assert lib.moe_block_backward_saved(*ins, sv, sb, T, d, d_ff, n, K, B.MOE_BF16, eps,
+                                            *grads) == B.MOE_ERR_INVALID_ARGUMENT
+        assert lib.moe_block_forward_train(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d,
+                                           d_ff, n, K, B.MOE_BF16, eps, FAKE * 64, sv, sb, ws,
+                                           1 << 30, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_block_backward(*ins, T, d, d_ff, n, K, B.MOE_F32, 1e-5,
+                                  *grads) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_block_backward_saved(*ins, None, sb, T, d, d_ff, n, K, B.MOE_BF16, 1e-5,
+                                        *grads) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_block_forward_train(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d,
+                                       d_ff, n, K, B.MOE_BF16, 1e-5, FAKE * 64, sv, sb - 1, ws,
+                                       1 << 30, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
