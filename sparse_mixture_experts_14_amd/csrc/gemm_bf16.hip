@@ -61,6 +61,8 @@ template <int NWV>
 using Square = Shape<256, 256, 2, NWV / 2>;  // full row tiles
 template <int NWV>
 using Wide = Shape<128, 512, 1, NWV>;        // an expert's last row tile of <= 128 rows
+template <int NWV>
+using Narrow = Shape<64, 512, 1, NWV>;       // ... of <= 64 rows: half the MFMA work
 constexpr int STAGE_MAX = (128 + 512) * ROW_BYTES;  // the larger (wide) stage
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -129,7 +131,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     constexpr int A_BYTES = BM * KD * 2;          // A tile of one stage
     constexpr int STAGE_BYTES = (BM + BN) * KD * 2;
     constexpr int KS = KD / 16;                   // MFMA sub-steps per step
-    static_assert(TM == 4 && (TN == 4 || TN == 2), "waves of 128 x 128 or 128 x 64");
+    static_assert((TM == 4 || TM == 2) && (TN == 4 || TN == 2),
+                  "waves of 128 or 64 rows x 128 or 64 columns");
     static_assert(STAGE_BYTES <= STG, "stage fits (STG: bytes of each stage object)");
     static_assert(!(GATEUP && (AKR || BKR)), "K-row operands only in plain products");
     static_assert(KD == BK || (KD == 32 && AKR && BKR), "32-deep steps: K-row operands only");
@@ -617,7 +620,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         t.row0 = start + nsq * SQ::BM;
         t.rows = end - t.row0;
         t.n0 = 2 * c * BNO_S;
-        tile_body<GATEUP, KTAIL, WD, STG, EPI>(t, S0, S1);
+        // the same tile slot; a tail of at most 64 rows runs on 64-row waves
+        if (t.rows <= Narrow<NWV>::BM)
+            tile_body<GATEUP, KTAIL, Narrow<NWV>, STG, EPI>(t, S0, S1);
+        else
+            tile_body<GATEUP, KTAIL, WD, STG, EPI>(t, S0, S1);
     }
 }
 
