@@ -525,7 +525,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // gate/up and the down projection may run wide tiles (larger stages)
     using SQ = Square<NWV>;
     using WD = Wide<NWV>;
-    constexpr bool WIDE_OK = GATEUP || (!BKR && EPI == 0);
+    constexpr bool WIDE_OK = true;
     constexpr int STG = WIDE_OK ? STAGE_MAX : SQ::STAGE_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t S0[STG];
     __shared__ __attribute__((aligned(1024))) uint8_t S1[STG];
@@ -547,9 +547,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     constexpr int BNO_S = GATEUP ? SQ::BN / 2 : SQ::BN;  // output columns per tile
     const int ntn_s = (N + BNO_S - 1) / BNO_S;  // square column tiles
     const int npair = (ntn_s + 1) / 2;           // column pairs = wide column tiles
-    // Wide tail tiles: gate/up for every tail of at most 128 rows; the down
-    // projection for tails of at most down_wide_max rows.
-    const int WIDE_MAX = GATEUP ? WD::BM : WIDE_OK ? down_wide_max : 0;
+    // Wide tail tiles: gate/up for every tail of at most 128 rows; the plain
+    // products for tails of at most down_wide_max rows.
+    const int WIDE_MAX = GATEUP ? WD::BM : down_wide_max;
     auto expert_tiles = [&](int m, int& nsq, int& nwide) {
         const int rem = m % SQ::BM;
         nsq = m / SQ::BM + (rem > WIDE_MAX ? 1 : 0);
@@ -622,9 +622,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         t.n0 = 2 * c * BNO_S;
         // the same tile slot; a tail of at most 64 rows runs on 64-row waves
         if (t.rows <= Narrow<NWV>::BM)
-            tile_body<GATEUP, KTAIL, Narrow<NWV>, STG, EPI>(t, S0, S1);
+            tile_body<GATEUP, KTAIL, Narrow<NWV>, STG, EPI, false, BKR>(t, S0, S1);
         else
-            tile_body<GATEUP, KTAIL, WD, STG, EPI>(t, S0, S1);
+            tile_body<GATEUP, KTAIL, WD, STG, EPI, false, BKR>(t, S0, S1);
     }
 }
 
@@ -678,13 +678,15 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, int64_t a_stride,
     const int mtn = (N1 + SQ::BM - 1) / SQ::BM, ntn = (N2 + SQ::BN - 1) / SQ::BN;
     const int per_e = mtn * ntn;
     const int tiles = n * per_e;
-    // each XCD takes one contiguous share; inside an expert, groups of GM
-    // row tiles, and inside a group the row tile varies fastest: the group's
-    // A panels stay in L2 while its B panels stream past them
-    const int per_xcd = (tiles + 7) / 8;
-    const int jx = (int)(blockIdx.x >> 3);
-    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
-    if (jx >= per_xcd || L0 >= tiles) return;
+    // Tile L runs as block L, on XCD L % 8: every XCD gets an equal share of
+    // every expert's tiles.  A tile's K length is its expert's row count, so
+    // a contiguous share per XCD (as in the forward) would load the XCD that
+    // holds the largest expert with its whole work (four times the mean under
+    // the skewed routing where one expert takes half the rows).  Inside an
+    // expert, groups of GM row tiles, and inside a group the row tile varies
+    // fastest.
+    const int L0 = (int)blockIdx.x;
+    if (L0 >= tiles) return;
     const int e = L0 / per_e, rem = L0 - e * per_e;
     const int pbeg = offsets[e], pend = offsets[e + 1];
     TileArgs t;
@@ -828,14 +830,17 @@ hipError_t launch_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1, co
     const int64_t blocks = (mslots * ((N + SQ::BN - 1) / SQ::BN) * splits + 7) / 8 * 8;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int64_t stride = A_rows * (int64_t)N;
+    // expert tails of at most 64 rows run as 64 x 512 tiles (a square tile
+    // would leave three quarters of its MFMA rows idle); 128 x 512 tiles for
+    // tails of 65..128 rows measured no faster here than square ones
     if (Kdim % BK)
         hipLaunchKernelGGL((gemm_bf16_kernel<false, true, NWV, EPI, true>),
                            dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
-                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split);
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<false, false, NWV, EPI, true>),
                            dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
-                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split);
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64);
     return hipGetLastError();
 }
 
