@@ -505,7 +505,15 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
                     else
                         out = static_cast<uint8_t*>(t.Cout) +
                               ((int64_t)(t.row0 + row) * N + col) * ES;
-                    *reinterpret_cast<u32x4_t*>(out) = v;
+                    // Streaming stores: the output is not read again by this
+                    // kernel, and its lines need not displace operand panels
+                    // from L2 (weight gradients 4-6% faster, the stack layer's
+                    // forward 0.5%).  The 32-deep weight-gradient tiles (a few
+                    // rows per expert: a pure write) measured 2% slower so.
+                    if constexpr (KD == 32)
+                        *reinterpret_cast<u32x4_t*>(out) = v;
+                    else
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out));
                 }
             }
         }
