@@ -90,6 +90,16 @@ def test_backward_tile_boundaries_and_empty_expert():
     assert counts.tolist() == sizes
 
 
+def test_backward_short_expert_tails():
+    # expert tails of 1, 63, 64, 65, 127 and 128 rows past whole 256-row
+    # tiles: the 64 x 512 tail tiles of the K-row products (at most 64
+    # rows) and the square tiles above them
+    sizes = [257, 319, 320, 321, 383, 384, 64, 1]
+    L, _ = steered_layer(sizes, 256, 1032, seed=33)
+    _, counts = check_backward(L, 1, _dy(sum(sizes), 256, 133), "short-tails")
+    assert counts.tolist() == sizes
+
+
 def test_backward_mixtral_shape_dx():
     # full hidden and expert widths at decode size: every dx row against the
     # oracle, the router-gradient rows summing to zero, empty experts zero
