@@ -62,6 +62,14 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.handle)
 
 
+def step_percentiles(marks) -> dict:
+    """p10 / p50 / p90 of the per-step times between consecutive events."""
+    import numpy as np
+    per = np.array([a.elapsed_time(b) for a, b in zip(marks[:-1], marks[1:])])
+    return {q: round(float(np.percentile(per, v)), 5)
+            for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
 def kernel_source_sha(files) -> str:
     h = hashlib.sha256()
     for f in files:
@@ -310,16 +318,15 @@ def bench_backward(args, w, dev, train=False):
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
     every = max(1, args.stage_every)
     kev = {s: (HipEvent(), HipEvent()) for s in range(args.steps) if s % every == 0}
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    marks[0].record()
     for s in range(args.steps):
         step(kev.get(s))
-    end.record()
+        marks[s + 1].record()
     torch.cuda.synchronize()
     moe._lib.set_stage_events_raw("bwd_wgrad")
-    ms = start.elapsed_time(end) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     k_ms = [a.elapsed_ms(b) / 3.0 for (a, b) in kev.values()]  # three launches per stage
     k_avg = sum(k_ms) / len(k_ms)
     if stack:
@@ -366,6 +373,7 @@ def bench_backward(args, w, dev, train=False):
                    "n": w.n, "K": w.K, "dtype": w.dtype,
                    **({"layers": 1, "layer": 0, "eps": eps} if stack else {})},
         "roofline": roof,
+        "step_ms": step_percentiles(marks),
         # backward: gate/up recompute 4, r = W2^T dy 2, dx 4, weight gradients
         # 6; training step: forward 6 + backward without recompute 12 (x A d d_ff)
         "step_tflops": round(18.0 * A * w.d * w.d_ff / (ms * 1e-3) / 1e12 if train else
@@ -468,16 +476,15 @@ def main():
     every = max(1, args.stage_every)
     timed = [s for s in range(args.steps) if s % every == 0]
     kev = {s: [(HipEvent(), HipEvent()) for _ in range(nl)] for s in timed}
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    marks[0].record()
     for s in range(args.steps):
         step(kev.get(s))
-    end.record()
+        marks[s + 1].record()
     torch.cuda.synchronize()
     moe._lib.set_stage_events_raw("gate_up")
-    ms = start.elapsed_time(end) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     k_ms = [a.elapsed_ms(b) for st in kev.values() for (a, b) in st]
     k_avg = sum(k_ms) / len(k_ms)
     counts = lay.counts.cpu().tolist()
@@ -515,6 +522,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "n": w.n, "K": w.K,
                    "layers": w.layers, "dtype": w.dtype},
         "roofline": roof,
+        "step_ms": step_percentiles(marks),
     }
     # whole-step rate over the touched weights, for context
     if w.name in ("decode",):
