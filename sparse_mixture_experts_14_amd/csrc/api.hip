@@ -119,7 +119,7 @@ Plan choose_plan(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_d
 }
 
 struct Layout {
-    size_t idx, gate, offsets, perm, inv, u, H, O, total;
+    size_t idx, gate, offsets, perm, inv, meta, u, H, O, total;
 };
 
 Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt) {
@@ -133,6 +133,7 @@ Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtyp
     L.offsets = o; o = align256(o + (size_t)(n + 1) * 4);
     L.perm = o;    o = align256(o + A * 4);
     L.inv = o;     o = align256(o + A * 4);
+    L.meta = o;    o = align256(o + 2 * 4);  // (R0, Sr) of the tiled down projection
     L.u = o;       o = align256(o + (size_t)T * (size_t)d * es);
     L.H = o;       o = align256(o + A * (size_t)d_ff * es);
     L.O = o;       o = align256(o + (size_t)S * A * (size_t)d * 4);
@@ -361,6 +362,7 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     const void* act = block ? u : x;
     int splits = 1;
+    int* split_meta = nullptr;  // the tiled down projection's (R0, Sr), for the combine
     const int cus = device_cus();
     SkinnyShape sk_gu{7, 1}, sk_dn{7, 1};
     if (bf16 && plan.skinny) {
@@ -368,8 +370,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
         sk_dn = choose_skinny(n, d, d_ff, plan.down_splits, cus);
         splits = sk_dn.splits;
     } else if (bf16) {
-        splits = moe::tiled_down_splits((int64_t)A, n, (int)d, (int)d_ff, cus,
-                                        requested_down_splits(T, K));
+        splits = requested_down_splits(T, K);  // at most; the kernel picks Sr from the tiles
+        split_meta = reinterpret_cast<int*>(ws + L.meta);
     }
     for (int stage = MOE_STAGE_GATE_UP; stage <= MOE_STAGE_DOWN; ++stage) {
         const bool gu = stage == MOE_STAGE_GATE_UP;
@@ -406,7 +408,7 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                                   static_cast<const uint16_t*>(b1),
                                                   static_cast<const uint16_t*>(b3), offsets, n,
                                                   (int64_t)A, kdim, ndim, c_out,
-                                                  gu ? 1 : splits, s);
+                                                  gu ? 1 : splits, cus, split_meta, s);
         }
         mark(g_ev_end[stage]);
         if (err != hipSuccess) return hip_fail(err, gu ? "gate/up GEMM launch" : "down GEMM launch");
@@ -414,7 +416,7 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     mark(g_ev_start[MOE_STAGE_COMBINE]);
     if (err == hipSuccess)
         err = moe::launch_combine(bf16, block, O, (int64_t)A, splits, inv, gate, T, K, (int)d, x,
-                                  y, s);
+                                  y, split_meta, s);
     mark(g_ev_end[MOE_STAGE_COMBINE]);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
     g_last_error[0] = '\0';

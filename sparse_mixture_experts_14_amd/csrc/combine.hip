@@ -6,10 +6,11 @@
 // back to their tokens' original positions.
 //
 // One thread per 4 output columns (a workgroup covers 1024 columns of one
-// token).  Each token gathers its K expert rows (fp32, possibly split into S partial
-// sums of the down projection) and sums them in a fixed order -- partials in
-// split order, then slots in k order -- so the result is deterministic and no
-// atomics are needed.  The sum is rounded once into the output dtype (RNE).
+// token).  Each token gathers its K expert rows (fp32, possibly split into
+// partial sums of the down projection: S for every row, or, after the tiled
+// down projection, Sr for the rows from R0 on and one before) and sums them
+// in a fixed order -- partials in split order, then slots in k order -- so
+// the result is deterministic and no atomics are needed.  The sum is rounded once into the output dtype (RNE).
 // The residual variant adds x_t (fp32) before that single rounding.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -21,11 +22,14 @@ template <typename TOut, bool RESID>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ O, int64_t A, int S, const int32_t* __restrict__ inv,
     const float* __restrict__ gate, int K, int d, const TOut* __restrict__ resid,
-    TOut* __restrict__ y) {
+    TOut* __restrict__ y, const int* __restrict__ split_meta) {
     const int cb = (d + 1023) / 1024;  // workgroups per token
     const int64_t t = blockIdx.x / cb;
     const int64_t split_stride = A * (int64_t)d;
     const int c = (int)(blockIdx.x % cb) * 1024 + threadIdx.x * 4;
+    // rows from R0 on hold Sr partial sums, the rows before it one
+    const int R0 = split_meta ? split_meta[0] : 0;
+    const int Sr = split_meta ? split_meta[1] : S;
     if (c < d) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k = 0; k < K; ++k) {
@@ -33,7 +37,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
             const float g = gate[t * K + k];
             const float* __restrict__ row = O + pos * (int64_t)d + c;
             float4 o = *reinterpret_cast<const float4*>(row);
-            for (int s = 1; s < S; ++s) {
+            const int np = pos >= R0 ? Sr : 1;
+            for (int s = 1; s < np; ++s) {
                 const float4 p = *reinterpret_cast<const float4*>(row + s * split_stride);
                 o.x += p.x;
                 o.y += p.y;
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int S,
                           const int32_t* inv, const float* gate, int64_t T, int K, int d,
-                          const void* x, void* y, hipStream_t s) {
+                          const void* x, void* y, const int* split_meta, hipStream_t s) {
     const int64_t cb = (d + 1023) / 1024;
     if (T * cb > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(T * cb));
@@ -87,20 +92,20 @@ hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int 
         if (resid)
             hipLaunchKernelGGL((combine_kernel<uint16_t, true>), grid, block, 0, s, O, A, S,
                                inv, gate, K, d, static_cast<const uint16_t*>(x),
-                               static_cast<uint16_t*>(y));
+                               static_cast<uint16_t*>(y), split_meta);
         else
             hipLaunchKernelGGL((combine_kernel<uint16_t, false>), grid, block, 0, s, O, A,
                                S, inv, gate, K, d, static_cast<const uint16_t*>(x),
-                               static_cast<uint16_t*>(y));
+                               static_cast<uint16_t*>(y), split_meta);
     } else {
         if (resid)
             hipLaunchKernelGGL((combine_kernel<float, true>), grid, block, 0, s, O, A, S,
                                inv, gate, K, d, static_cast<const float*>(x),
-                               static_cast<float*>(y));
+                               static_cast<float*>(y), split_meta);
         else
             hipLaunchKernelGGL((combine_kernel<float, false>), grid, block, 0, s, O, A, S,
                                inv, gate, K, d, static_cast<const float*>(x),
-                               static_cast<float*>(y));
+                               static_cast<float*>(y), split_meta);
     }
     return hipGetLastError();
 }

@@ -569,7 +569,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                       const uint16_t* __restrict__ B3, const int32_t* __restrict__ offsets,
                       int n, int Kdim, int N, void* __restrict__ Cout, int GM, int splits,
                       int64_t split_stride, int b_split = 0, void* __restrict__ Cout2 = nullptr,
-                      int down_wide_max = 0) {
+                      int down_wide_max = 0, int cus = 0, int* __restrict__ split_meta = nullptr) {
     // gate/up and the down projection may run wide tiles (larger stages)
     using SQ = Square<NWV>;
     using WD = Wide<NWV>;
@@ -609,20 +609,81 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         int a, c;
         tiles += expert_tiles(offsets[q + 1] - offsets[q], a, c);
     }
-    const int per_xcd = (tiles * splits + 7) / 8;
-    const int jx = (int)(blockIdx.x >> 3);
-    const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
-    if (jx >= per_xcd || L0 >= tiles * splits) return;
-    const int ks = L0 / tiles;  // K split of this block
-    int L = L0 - ks * tiles;
-    int e = 0, start = offsets[0], nsq = 0, nwide = 0;
-    for (;; ++e) {  // ends: L < tiles
-        const int cnt = expert_tiles(offsets[e + 1] - start, nsq, nwide);
+    // This block's tile L among the tiles of rows [lo, hi), and its K split
+    // ks of nsplit.
+    int lo = offsets[0], hi = offsets[n], ks = 0, nsplit = splits, L = 0;
+    if (cus > 0) {
+        // Split only the remainder (the down projection): the tiles fill
+        // tiles / cus whole rounds of the CUs, plus r = tiles % cus left over.
+        // The last row tiles in expert order (at least r tiles, whole rows of
+        // tiles, from row R0 on) run as Sr K splits each, Sr = cus / their
+        // count (at most `splits`), so they make one short round instead of
+        // a mostly idle full one; every other tile runs its whole K once.
+        // Rows >= R0 hold Sr partial sums, the rest one; (R0, Sr) go to
+        // split_meta for the combine.
+        int R0 = offsets[n], Sr = 1, Trem = 0;
+        const int r = tiles % cus;
+        if (r > 0 && splits > 1) {
+            for (int q = n - 1; q >= 0 && Trem < r; --q) {
+                int nsq_q, nw_q;
+                const int s0 = offsets[q];
+                expert_tiles(offsets[q + 1] - s0, nsq_q, nw_q);
+                if (nw_q) {  // the tail tile (its squares are all full)
+                    Trem += npair;
+                    R0 = s0 + nsq_q * SQ::BM;
+                }
+                if (Trem >= r) break;
+                const int take = min((r - Trem + ntn_s - 1) / ntn_s, nsq_q);
+                Trem += take * ntn_s;
+                if (take > 0) R0 = s0 + (nsq_q - take) * SQ::BM;
+            }
+            Sr = min(splits, cus / Trem);
+            if (Sr < 2) {
+                Sr = 1;
+                R0 = offsets[n];
+                Trem = 0;
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            split_meta[0] = R0;
+            split_meta[1] = Sr;
+        }
+        // blocks [0, 8 per_xcd): the whole-K tiles, a contiguous eighth per
+        // XCD as below; then the split tiles, consecutive ones on different
+        // XCDs (block b runs on XCD b % 8)
+        const int Tdp = tiles - Trem;
+        const int per_xcd = (Tdp + 7) / 8;
+        if ((int)blockIdx.x < 8 * per_xcd) {
+            L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+            if (L >= Tdp) return;
+            hi = R0;
+            nsplit = 1;
+        } else {
+            const int u = (int)blockIdx.x - 8 * per_xcd;
+            if (u >= Trem * Sr) return;
+            ks = u / Trem;
+            L = u - ks * Trem;
+            lo = R0;
+            nsplit = Sr;
+        }
+    } else {
+        const int per_xcd = (tiles * splits + 7) / 8;
+        const int jx = (int)(blockIdx.x >> 3);
+        const int L0 = (int)(blockIdx.x & 7) * per_xcd + jx;
+        if (jx >= per_xcd || L0 >= tiles * splits) return;
+        ks = L0 / tiles;  // K split of this block
+        L = L0 - ks * tiles;
+    }
+    // the expert of tile L, over the rows of [lo, hi) (R0 is a row-tile
+    // boundary of its expert, so both sides keep the expert's own tiling)
+    int e = 0, start = 0, end = 0, nsq = 0, nwide = 0;
+    for (;; ++e) {  // ends: L < the tiles of [lo, hi)
+        start = max(offsets[e], lo);
+        end = min(offsets[e + 1], hi);
+        const int cnt = expert_tiles(max(0, end - start), nsq, nwide);
         if (L < cnt) break;
         L -= cnt;
-        start = offsets[e + 1];
     }
-    const int end = offsets[e + 1];
     // row group: all but the last hold GM square row tiles and no wide tile
     const int ngroups = max(1, (nsq + GM - 1) / GM);
     int g = min(L / (GM * ntn_s), ngroups - 1);
@@ -655,7 +716,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP || EPI == 2 ? 2 : 4);
     t.Cout2 = Cout2;
     const int nk_all = (Kdim + BK - 1) / BK;
-    const int per_split = (nk_all + splits - 1) / splits;
+    const int per_split = (nk_all + nsplit - 1) / nsplit;
     t.k_begin = min(nk_all, ks * per_split);
     t.k_end = min(nk_all, t.k_begin + per_split);
     if (L < gm * ncol) {
@@ -680,14 +741,18 @@ template <bool GATEUP, int NWV = 4, int EPI = 0>
 hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* perm, int K,
                         const uint16_t* B1, const uint16_t* B3, const int32_t* offsets, int n,
                         int64_t A_rows, int Kdim, int N, void* C, int GM, int splits,
-                        hipStream_t s, void* C2 = nullptr, int down_wide_max = 0) {
+                        hipStream_t s, void* C2 = nullptr, int down_wide_max = 0, int cus = 0,
+                        int* split_meta = nullptr) {
     using SQ = Square<NWV>;
     constexpr int BNO = GATEUP ? SQ::BN / 2 : SQ::BN;
     // upper bound of the tiles: each expert's last row tile may be partial
-    // (a wide tile never has more column tiles than a square one)
+    // (a wide tile never has more column tiles than a square one); with the
+    // remainder split (cus > 0), the whole-K tiles plus at most cus split ones
     const int64_t mslots = A_rows / SQ::BM + n;
     const int64_t ntn = (N + BNO - 1) / BNO;
-    const int64_t blocks = (mslots * ntn * splits + 7) / 8 * 8;
+    const int64_t blocks =
+        cus > 0 ? (mslots * ntn + 7) / 8 * 8 + (cus + 7) / 8 * 8 : (mslots * ntn * splits + 7) / 8 * 8;
+    if (cus > 0 && (GATEUP || !split_meta)) return hipErrorInvalidValue;
     if (blocks > 0x7fffffff || splits < 1 || (GATEUP && splits != 1))
         return hipErrorInvalidConfiguration;
     const bool ktail = Kdim % BK != 0;
@@ -695,11 +760,11 @@ hipError_t launch_tiled(const uint16_t* A, int64_t A_src_rows, const int32_t* pe
     if (ktail)
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, true, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride, 0, C2, down_wide_max);
+                           N, C, GM, splits, stride, 0, C2, down_wide_max, cus, split_meta);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<GATEUP, false, NWV, EPI>), dim3((unsigned)blocks),
                            dim3(NWV * 64), 0, s, A, A_src_rows, perm, K, B1, B3, offsets, n, Kdim,
-                           N, C, GM, splits, stride, 0, C2, down_wide_max);
+                           N, C, GM, splits, stride, 0, C2, down_wide_max, cus, split_meta);
     return hipGetLastError();
 }
 
@@ -801,8 +866,9 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
                                   const int32_t* perm, int K, const uint16_t* B1,
                                   const uint16_t* B3, const int32_t* offsets, int n,
                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
-                                  hipStream_t s) {
-    if (!tiled_fits(A_src_rows, Kdim, N)) return hipErrorInvalidValue;
+                                  int cus, int* split_meta, hipStream_t s) {
+    if (!tiled_fits(A_src_rows, Kdim, N) || (!gateup && (cus < 1 || !split_meta)))
+        return hipErrorInvalidValue;
     // Gate/up: four waves of 128 x 128.  Down: eight waves of 128 x 64 (two
     // per SIMD), measured 2% faster there and 3.5% slower on gate/up.
     const int GM = 8;
@@ -810,9 +876,10 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
         return launch_tiled<true, 4>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
                                      C, GM, 1, s);
     // Down tails of at most 128 rows run wide as on gate/up (measured: 1%
-    // faster on the 32-layer stack at T = 2048, unchanged at T = 4096).
+    // faster on the 32-layer stack at T = 2048, unchanged at T = 4096).  Up
+    // to `splits` K splits for the last round's tiles only (see the kernel).
     return launch_tiled<false, 8>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
-                                  C, GM, splits, s, nullptr, 128);
+                                  C, GM, splits, s, nullptr, 128, cus, split_meta);
 }
 
 }  // namespace moe

@@ -22,13 +22,16 @@ hipError_t launch_gemm_f32(bool gateup, const float* A, const int32_t* perm, int
 
 // bf16 MFMA grouped GEMMs, LDS-tiled (many rows per expert).  A has
 // A_src_rows rows of Kdim elements (x, u or H).
-// The down projection (gateup false) may split K into `splits` partial sums,
-// written `A_rows * N` elements apart; gate/up takes splits = 1.
+// The down projection (gateup false) splits the K range of its last round's
+// tiles (the rows from R0 on) into Sr <= `splits` partial sums, written
+// `A_rows * N` elements apart (buffer 0 holds every row's first or only
+// sum); it writes (R0, Sr) to split_meta[0..1] for the combine.  `cus` is
+// the CU count of the device.  Gate/up takes splits = 1 and no split_meta.
 hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                   const int32_t* perm, int K, const uint16_t* B1,
                                   const uint16_t* B3, const int32_t* offsets, int n,
                                   int64_t A_rows, int Kdim, int N, void* C, int splits,
-                                  hipStream_t s);
+                                  int cus, int* split_meta, hipStream_t s);
 // Gate/up grouped GEMM that stores the pre-activations instead of H:
 // AB[p] = [a | b] (bf16, 2 N columns), a = u_p W1_e^T, b = u_p W3_e^T.
 hipError_t launch_gemm_bf16_gateup_ab(const uint16_t* A, int64_t A_src_rows, const int32_t* perm,
@@ -91,10 +94,12 @@ hipError_t launch_gemm_bf16_skinny(bool gateup, const uint16_t* A, int64_t A_src
 bool skinny_fits(int64_t A_src_rows, int64_t A_rows, int64_t Kdim, int64_t N, int splits);
 int skinny_splits_used(int Kdim, int splits);
 
-// y = sum_k gate * (sum over S splits of O) (+ x), rounded once.
+// y = sum_k gate * (sum over S splits of O) (+ x), rounded once.  With
+// split_meta (R0, Sr) from the tiled down projection, rows >= R0 hold Sr
+// partial sums and the others one; without it every row holds S.
 hipError_t launch_combine(bool bf16, bool resid, const float* O, int64_t A, int S,
                           const int32_t* inv, const float* gate, int64_t T, int K, int d,
-                          const void* x, void* y, hipStream_t s);
+                          const void* x, void* y, const int* split_meta, hipStream_t s);
 
 // ---- backward pass (backward.hip) ---------------------------------------------
 // Per assignment row p (a = perm[p]) from [a | b] = AB[p] and the bf16

@@ -20,10 +20,19 @@ def test_decode_all_tokens():
     rep, _ = check_layer(L, 2, label="decode")
 
 
+def split_tail_tokens(L, K, n, count):
+    """The last tokens routed to expert n - 1: their assignment rows end the
+    expert order, where the down projection splits its last round's tiles
+    into K-split partial sums."""
+    idx, _ = moe.route(L["x"], L["Wg"], K)
+    return np.flatnonzero((P.to_np(idx) == n - 1).any(1))[-count:]
+
+
 def test_prefill_sampled():
     w = W.WORKLOADS["prefill"]
     L = W.make_layer(w, device="cuda")
-    rows = np.sort(np.random.default_rng(0).choice(w.T, 192, replace=False))
+    rows = np.union1d(np.random.default_rng(0).choice(w.T, 192, replace=False),
+                      split_tail_tokens(L, w.K, w.n, 32))
     check_layer(L, 2, rows=rows, label="prefill")
 
 
@@ -51,4 +60,8 @@ def test_stack_layer_sampled(layer):
         # a deeper layer sees a wider residual stream; its own seeded input
         L["x"] = W.random_tokens(w.T, w.d, seed=500 + layer, device="cuda", std=2.5)
     rows = np.sort(np.random.default_rng(layer).choice(w.T, 96, replace=False))
+    if layer == 0:  # routing is on the normalised input; its order matches x's
+        u = L["x"].float()
+        u = (u * torch.rsqrt(u.pow(2).mean(1, keepdim=True) + w.eps)).to(L["x"].dtype)
+        rows = np.union1d(rows, split_tail_tokens({**L, "x": u}, w.K, w.n, 24))
     check_layer(L, 2, block=True, eps=w.eps, rows=rows, label=f"stack-layer{layer}")
