@@ -177,8 +177,8 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // moe_block_forward_train is exactly the first seven regions (idx .. U), at
 // the same offsets.
 struct BwdLayout {
-    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, U, DU, SC,
-        total;
+    size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, U, meta,
+        DU, SC, total;
 };
 
 constexpr int kBwdMaxSplits = 4;  // K splits of the tiled dx product
@@ -232,6 +232,8 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.AB = o;      o = align256(o + A * 2 * ff * 2);
     // stack layer: u = bf16(RMSNorm(x)) (also part of the saved state)
     L.U = o;       o = align256(o + (size_t)T * dd * 2);
+    // (the saved state ends here)
+    L.meta = o;    o = align256(o + 2 * 4);  // (R0, Sr) of the tiled dx product
     L.DX = o;      o = align256(o + dx_parts * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
     L.DYG = o;     o = align256(o + A * dd * 2);
@@ -540,10 +542,13 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
     // the forward's GEMM family: MFMA tiles, or weight streams for few rows
     // per expert
     const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
-    // (the cost model's choice measured best: 4 splits at T = 4096)
-    int dx_splits = moe::tiled_down_splits(A, n, D, 2 * F, cus, kBwdMaxSplits);
+    // the tiled dx product splits K for its last round's tiles only (at most
+    // kBwdMaxSplits), recording (R0, Sr) for the token kernel
+    int dx_splits = kBwdMaxSplits;
+    int* dx_meta = reinterpret_cast<int*>(ws + L.meta);
     SkinnyShape st_r{7, 1}, st_x{7, 1};
     if (plan.skinny) {
+        dx_meta = nullptr;
         const int cap = stream_split_cap(A, d, d_ff);
         st_r = choose_stream(n, d_ff, d, cap, cus);
         st_x = choose_stream(n, d, 2 * d_ff, cap, cus);
@@ -585,7 +590,7 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
              "SwiGLU backward");
     } else {
         STEP(moe::launch_gemm_bf16_krow(DYG, A, w2b, nullptr, D, offsets, n, D, F, DH, true, 1,
-                                        s),
+                                        cus, nullptr, s),
              "dh product");
         STEP(moe::launch_bwd_swiglu(AB, DH, nullptr, 1, perm, gate, A, F, dg, DADB, GH, s),
              "SwiGLU backward");
@@ -600,13 +605,13 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
              "dx product");
     else
         STEP(moe::launch_gemm_bf16_krow(DADB, A, w1b, w3b, F, offsets, n, 2 * F, D, DX, false,
-                                        dx_splits, s),
+                                        dx_splits, cus, dx_meta, s),
              "dx product");
     // router gradient, dx back in token order, dW_g
     STEP(moe::launch_bwd_token(static_cast<const uint16_t*>(w_g), idx, gate, dg, DX, dx_splits,
                                A, inv, T, K, n, D, dl,
                                block ? nullptr : static_cast<uint16_t*>(dx), block ? DU : nullptr,
-                               s),
+                               dx_meta, s),
          "token gradients");
     if (block)  // through the normalisation, plus the residual
         STEP(moe::launch_bwd_rms(x_in, static_cast<const uint16_t*>(dy), DU, T, D, eps,

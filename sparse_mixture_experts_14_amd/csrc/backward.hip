@@ -104,7 +104,11 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
     const uint16_t* __restrict__ wg, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const float* __restrict__ dg, const float* __restrict__ DX,
     int S, int64_t split_stride, const int32_t* __restrict__ inv, int K, int n, int d,
-    float* __restrict__ dl, uint16_t* __restrict__ dx, float* __restrict__ dx32) {
+    float* __restrict__ dl, uint16_t* __restrict__ dx, float* __restrict__ dx32,
+    const int* __restrict__ split_meta) {
+    // rows from R0 on hold Sr partial sums, the rows before it one
+    const int R0 = split_meta ? split_meta[0] : 0;
+    const int Sr = split_meta ? split_meta[1] : S;
     __shared__ float sdl[64];
     const int64_t t = blockIdx.x;
     if (threadIdx.x < 64) sdl[threadIdx.x] = 0.0f;
@@ -126,9 +130,11 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
             for (int u = 0; u < 4; ++u) s[u] = fmaf(bf(wg[(int64_t)(k + u) * n + i]), sdl[i], s[u]);
         }
         for (int j = 0; j < K; ++j) {
-            const float* src = DX + (int64_t)inv[t * K + j] * d + k;
+            const int pos = inv[t * K + j];
+            const float* src = DX + (int64_t)pos * d + k;
+            const int np = pos >= R0 ? Sr : 1;
 #pragma unroll 4
-            for (int q = 0; q < S; ++q) {
+            for (int q = 0; q < np; ++q) {
                 const float4 v = *reinterpret_cast<const float4*>(src + q * split_stride);
                 s[0] += v.x;
                 s[1] += v.y;
@@ -325,13 +331,13 @@ hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,
                             const float* dg, const float* DX, int S, int64_t A,
                             const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
-                            uint16_t* dx, float* dx32, hipStream_t s) {
+                            uint16_t* dx, float* dx32, const int* split_meta, hipStream_t s) {
     if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
     // few tokens: spread each token's columns over several blocks
     const int ycols = (d + 1023) / 1024;
     const int gy = T >= 1024 ? 1 : ycols;
     hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)T, (unsigned)gy), dim3(256), 0, s, wg,
-                       idx, gate, dg, DX, S, A * d, inv, K, n, d, dl, dx, dx32);
+                       idx, gate, dg, DX, S, A * d, inv, K, n, d, dl, dx, dx32, split_meta);
     return hipGetLastError();
 }
 

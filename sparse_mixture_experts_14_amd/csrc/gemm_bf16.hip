@@ -837,31 +837,6 @@ bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N) {
     return A_src_rows * Kdim * 2 < lim && N * Kdim * 2 < lim;
 }
 
-int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_splits) {
-    // Expected tiles: every expert's last row tile is half full on average.
-    const int64_t mt = (A_rows + 255) / 256 + n / 2;
-    const int64_t tiles = mt * ((N + 255) / 256);
-    if (tiles <= 0 || Kdim < 64 * 2) return 1;
-    // Time in units of one full-K tile round: S splits run ceil(S tiles /
-    // cus) rounds of 1/S-length tiles, and each split past the first writes
-    // and the combine reads another A x N fp32 partial.  Calibration
-    // (measured): a 64-deep K step of a tile round takes ~2 us, the partial
-    // traffic moves at ~5 bytes/ps.
-    const double unit_us = (double)((Kdim + 63) / 64) * 2.0;
-    const double partial_us = (double)A_rows * (double)N * 8.0 / 5.0e6;
-    int best = 1;
-    double best_t = 1e300;
-    for (int S = 1; S <= max_splits && S <= 4; ++S) {
-        const int64_t rounds = (tiles * S + cus - 1) / cus;
-        const double t = (double)rounds / S * unit_us + (S - 1) * partial_us;
-        if (t < best_t * 0.99) {  // a split must win by 1%
-            best_t = t;
-            best = S;
-        }
-    }
-    return best;
-}
-
 hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_rows,
                                   const int32_t* perm, int K, const uint16_t* B1,
                                   const uint16_t* B3, const int32_t* offsets, int n,
@@ -939,11 +914,16 @@ hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uin
 template <int NWV, int EPI>
 hipError_t launch_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1, const uint16_t* B3,
                        int b_split, const int32_t* offsets, int n, int Kdim, int N, void* C,
-                       int splits, hipStream_t s) {
+                       int splits, int cus, int* split_meta, hipStream_t s) {
     using SQ = Square<NWV>;
     const int64_t mslots = A_rows / SQ::BM + n;
-    const int64_t blocks = (mslots * ((N + SQ::BN - 1) / SQ::BN) * splits + 7) / 8 * 8;
+    const int64_t ntn = (N + SQ::BN - 1) / SQ::BN;
+    // with split_meta: whole-K tiles plus at most cus split ones (see the kernel)
+    const int64_t blocks = split_meta ? (mslots * ntn + 7) / 8 * 8 + (cus + 7) / 8 * 8
+                                      : (mslots * ntn * splits + 7) / 8 * 8;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (split_meta && cus < 1) return hipErrorInvalidValue;
+    if (!split_meta) cus = 0;
     const int64_t stride = A_rows * (int64_t)N;
     // expert tails of at most 64 rows run as 64 x 512 tiles (a square tile
     // would leave three quarters of its MFMA rows idle); 128 x 512 tiles for
@@ -951,27 +931,31 @@ hipError_t launch_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1, co
     if (Kdim % BK)
         hipLaunchKernelGGL((gemm_bf16_kernel<false, true, NWV, EPI, true>),
                            dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
-                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64);
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64,
+                           cus, split_meta);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<false, false, NWV, EPI, true>),
                            dim3((unsigned)blocks), dim3(NWV * 64), 0, s, A, A_rows, nullptr, 1, B1,
-                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64);
+                           B3, offsets, n, Kdim, N, C, 8, splits, stride, b_split, nullptr, 64,
+                           cus, split_meta);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
                                  const uint16_t* B3, int b_split, const int32_t* offsets, int n,
                                  int Kdim, int N, void* C, bool bf16_out, int splits,
-                                 hipStream_t s) {
+                                 int cus, int* split_meta, hipStream_t s) {
     const int64_t lim = int64_t(1) << 31;
     if (N % 8 || Kdim % 8 || (B3 ? 2 * b_split != Kdim : b_split != Kdim) ||
         A_rows * Kdim * 2 >= lim || (int64_t)b_split * N * 2 >= lim || splits < 1 ||
-        (bf16_out && splits != 1))
+        (bf16_out && (splits != 1 || split_meta)))
         return hipErrorInvalidValue;
     // eight waves of 128 x 64 (measured 10% faster than four of 128 x 128 here)
     if (bf16_out)
-        return launch_krow<8, 2>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, s);
-    return launch_krow<8, 0>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, s);
+        return launch_krow<8, 2>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits,
+                                 cus, nullptr, s);
+    return launch_krow<8, 0>(A, A_rows, B1, B3, b_split, offsets, n, Kdim, N, C, splits, cus,
+                             split_meta, s);
 }
 
 }  // namespace moe

@@ -56,11 +56,14 @@ hipError_t launch_gemm_bf16_wgrad(const uint16_t* A, int64_t a_stride, const uin
 // of split s of A[p][k] W_e[k][c], over the rows p of each expert e, with
 // K-row weights: W_e = B1 + e b_split N for k < b_split and B3 + e b_split N
 // (row k - b_split) beyond (B3 NULL: Kdim = b_split).  C is fp32, or bf16
-// (rounded once) when bf16_out, which allows one split only.
+// (rounded once) when bf16_out, which allows one split only.  With
+// split_meta (fp32 only), only the last round's tiles -- the rows from R0 on
+// -- take Sr <= splits K splits, as in the tiled down projection, and
+// (R0, Sr) go to split_meta; without it every tile takes `splits`.
 hipError_t launch_gemm_bf16_krow(const uint16_t* A, int64_t A_rows, const uint16_t* B1,
                                  const uint16_t* B3, int b_split, const int32_t* offsets, int n,
-                                 int Kdim, int N, void* C, bool bf16_out, int splits,
-                                 hipStream_t s);
+                                 int Kdim, int N, void* C, bool bf16_out, int splits, int cus,
+                                 int* split_meta, hipStream_t s);
 // Weight-stream variant of launch_gemm_bf16_krow for few rows per expert:
 // fp32 partial sums C[s][p][c] (split stride A_rows N) over `splits` K
 // ranges (krow_stream_splits_used() tells how many a request produces),
@@ -71,10 +74,6 @@ hipError_t launch_gemm_bf16_krow_stream(const uint16_t* A, int64_t A_rows, const
                                         const int32_t* offsets, int n, int Kdim, int N,
                                         float* C, int splits, int waves, int cus,
                                         hipStream_t s);
-// K splits worth using for the tiled down projection on `cus` compute units
-// (at most min(max_splits, 4)): the count that minimises tile rounds per split
-// plus the cost of the extra fp32 partial sums.  Depends on sizes only.
-int tiled_down_splits(int64_t A_rows, int n, int N, int Kdim, int cus, int max_splits);
 // Whether the tiled kernels can take these sizes (32-bit buffer offsets).
 bool tiled_fits(int64_t A_src_rows, int64_t Kdim, int64_t N);
 
@@ -112,12 +111,13 @@ hipError_t launch_bwd_swiglu(const uint16_t* AB, const uint16_t* DH, const float
                              const int32_t* perm, const float* gate, int64_t A, int dff,
                              float* dg, uint16_t* DADB, uint16_t* GH, hipStream_t s);
 // Router-logit gradient dl[T][n] and dx_t = W_g dl + sum_j sum_s
-// DX[s][inv[t K + j]] (S K-split partials, split stride A d): bf16 dx, or
+// DX[s][inv[t K + j]] (K-split partials, split stride A d: S for every row,
+// or with split_meta (R0, Sr) Sr for rows >= R0 and one below): bf16 dx, or
 // fp32 dx32 when that is given.
 hipError_t launch_bwd_token(const uint16_t* wg, const int32_t* idx, const float* gate,
                             const float* dg, const float* DX, int S, int64_t A,
                             const int32_t* inv, int64_t T, int K, int n, int d, float* dl,
-                            uint16_t* dx, float* dx32, hipStream_t s);
+                            uint16_t* dx, float* dx32, const int* split_meta, hipStream_t s);
 // Stack layer: dx = dy + s (du - u (u . du) / d) per token (u = x s,
 // s = 1 / sqrt(mean(x^2) + eps)); scale[t] = s.
 hipError_t launch_bwd_rms(const uint16_t* x, const uint16_t* dy, const float* du, int64_t T,
