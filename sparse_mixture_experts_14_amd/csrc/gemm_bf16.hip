@@ -14,7 +14,8 @@
 //             W1 rows and the same W3 rows, so the SiLU*mul epilogue finds
 //             both accumulators in the same lane.
 //   down:     O[s][p][c] = sum over the K range of split s of H_p . W2_e[c]
-//             (fp32 partial sums; the combine stage adds the splits).
+//             (fp32; only the tiles of the last round -- rows from R0 on --
+//             are split along K, and the combine adds their partial sums).
 //
 // Tile shapes.  Gate/up: four waves, each holding a 128 x 128 fp32
 // accumulator (4 x 4 MFMA tiles of 32 x 32, 256 accumulators per lane, in
@@ -34,9 +35,15 @@
 // 16 consecutive rows hit distinct banks).  A stage is filled by buffer loads
 // with the LDS flag (global -> LDS, no registers, no LDS write instructions),
 // issued one step ahead during the first MFMAs of a step; one barrier per
-// step waits for them.  Rows past the tile are clamped to a valid row (never
+// step waits for them (gate/up also prefetches its weight rows into L2 two
+// steps ahead).  Rows past the tile are clamped to a valid row (never
 // stored); a K tail and the step past the end load through an out-of-range
-// offset, which writes zeros.
+// offset, which writes zeros.  Outputs leave through LDS as whole 16-byte
+// chunks of rows, with non-temporal stores.
+//
+// The same tile body also runs the backward's products with K-row operands
+// ([K][cols] tiles read with the transposing LDS read): r = dy W2_e, the dx
+// product and the weight gradients.
 #include "common.hpp"
 #include "kernels.hpp"
 
