@@ -119,7 +119,7 @@ Plan choose_plan(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_d
 }
 
 struct Layout {
-    size_t idx, gate, offsets, perm, inv, meta, u, H, O, total;
+    size_t idx, gate, offsets, perm, inv, meta, pcnt, u, H, O, total;
 };
 
 Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt) {
@@ -134,6 +134,7 @@ Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtyp
     L.perm = o;    o = align256(o + A * 4);
     L.inv = o;     o = align256(o + A * 4);
     L.meta = o;    o = align256(o + 2 * 4);  // (R0, Sr) of the tiled down projection
+    L.pcnt = o;    o = align256(o + (size_t)moe::permute_blocks((int64_t)A) * (size_t)n * 4);
     L.u = o;       o = align256(o + (size_t)T * (size_t)d * es);
     L.H = o;       o = align256(o + A * (size_t)d_ff * es);
     L.O = o;       o = align256(o + (size_t)S * A * (size_t)d * 4);
@@ -178,7 +179,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // the same offsets.
 struct BwdLayout {
     size_t idx, gate, offsets, perm, inv, AB, DX, dg, DYG, DH, DADB, GH, XG, dl, part, U, meta,
-        DU, SC, total;
+        pcnt, DU, SC, total;
 };
 
 constexpr int kBwdMaxSplits = 4;  // K splits of the tiled dx product
@@ -234,6 +235,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K) {
     L.U = o;       o = align256(o + (size_t)T * dd * 2);
     // (the saved state ends here)
     L.meta = o;    o = align256(o + 2 * 4);  // (R0, Sr) of the tiled dx product
+    L.pcnt = o;    o = align256(o + (size_t)moe::permute_blocks((int64_t)A) * (size_t)n * 4);
     L.DX = o;      o = align256(o + dx_parts * A * dd * 4);
     L.dg = o;      o = align256(o + A * 4);
     L.DYG = o;     o = align256(o + A * dd * 2);
@@ -359,7 +361,8 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     if (err != hipSuccess) return hip_fail(err, "router launch");
     mark(g_ev_start[MOE_STAGE_PERMUTE]);
     if (err == hipSuccess)
-        err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s);
+        err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s,
+                                  reinterpret_cast<int32_t*>(ws + L.pcnt));
     mark(g_ev_end[MOE_STAGE_PERMUTE]);
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     const void* act = block ? u : x;
@@ -561,7 +564,9 @@ moe_status_t layer_backward(const void* x, const void* w_g, const void* w1, cons
         STEP(moe::launch_router(true, block, x, w_g, T, D, n, K, eps, idx, gate,
                                 block ? U : nullptr, s),
              "router");
-        STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s), "permute");
+        STEP(moe::launch_permute(idx, A, n, offsets, perm, inv, nullptr, s,
+                                 reinterpret_cast<int32_t*>(ws + L.pcnt)),
+             "permute");
         if (plan.skinny) {
             const SkinnyShape sk = choose_skinny(n, d_ff, d, 1, cus);
             STEP(moe::launch_gemm_bf16_skinny(true, xb, T, perm, K, w1b, w3b, offsets, n, A, D,

@@ -13,7 +13,18 @@ hipError_t launch_router(bool bf16, bool norm, const void* x, const void* wg, in
 
 // Stable counting sort of A = T*K assignments by expert.
 hipError_t launch_permute(const int32_t* idx, int64_t A, int n, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s);
+                          int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s,
+                          int32_t* scratch = nullptr);
+// Many assignments run over several workgroups (blocks of permute_chunk(A)
+// assignments) when launch_permute gets scratch for permute_blocks(A) * n
+// per-block counts; fewer than kPermSplitMin stay in one workgroup.
+constexpr int64_t kPermSplitMin = 4096;
+constexpr int kPermMaxBlocks = 1024;
+inline int64_t permute_chunk(int64_t A) {  // a multiple of 1024, at most kPermMaxBlocks blocks
+    const int64_t c = (A + kPermMaxBlocks - 1) / kPermMaxBlocks;
+    return c <= 1024 ? 1024 : (c + 1023) / 1024 * 1024;
+}
+int permute_blocks(int64_t A);
 
 // fp32 grouped GEMMs (gate/up with SiLU*mul epilogue, or down).
 hipError_t launch_gemm_f32(bool gateup, const float* A, const int32_t* perm, int K,

@@ -8,7 +8,7 @@
 // that grouping: offsets[e] (first row of expert e), perm[pos] = assignment,
 // inv[assignment] = pos.  Within an expert, rows keep assignment order.
 //
-// One workgroup of 16 wavefronts; no atomics, so the result is deterministic.
+// Workgroups of 16 wavefronts; no atomics, so the result is deterministic.
 //   pass 1  wave w counts its contiguous segment of assignments per expert
 //           with one ballot per expert per 64 assignments (lane e keeps the
 //           count of expert e, n <= 64);
@@ -16,6 +16,11 @@
 //   pass 2  the wave re-reads its segment; an assignment's position is its
 //           expert's running base plus the number of lower lanes holding the
 //           same expert in this batch (popcount of the ballot below the lane).
+// Few assignments: one workgroup does all of it.  Many (given scratch for
+// the per-block counts): a first kernel counts each block of CH assignments
+// per expert; in the second, each block forms its experts' bases from the
+// counts of the blocks before it (fixed order), then runs the two passes on
+// its own block.  Both give the same, stable order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,19 +29,11 @@ namespace {
 
 constexpr int kPermWaves = 16;
 
-__global__ __launch_bounds__(kPermWaves* kWave) void permute_kernel(
-    const int32_t* __restrict__ idx, int64_t A, int n, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ counts) {
-    __shared__ int32_t cnt[kPermWaves][64];
-    __shared__ int32_t base[kPermWaves][64];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    // contiguous segment per wave, a multiple of 64 long
-    const int64_t per = ((A + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
-    const int64_t beg = min((int64_t)w * per, A);
-    const int64_t end = min(beg + per, A);
-
-    int32_t c = 0;  // lane e: count of expert e in this segment
+// Lane e of the calling wave: the number of assignments of expert e among
+// [beg, end) (0 for e >= n).
+__device__ __forceinline__ int32_t count_segment(const int32_t* __restrict__ idx, int64_t beg,
+                                                 int64_t end, int n, int lane) {
+    int32_t c = 0;
     for (int64_t a0 = beg; a0 < end; a0 += kWave) {
         const int64_t a = a0 + lane;
         const int v = a < end ? idx[a] : -1;
@@ -45,20 +42,80 @@ __global__ __launch_bounds__(kPermWaves* kWave) void permute_kernel(
             if (lane == e) c += __popcll(m);
         }
     }
-    if (lane < 64) cnt[w][lane] = lane < n ? c : 0;
+    return lane < n ? c : 0;
+}
+
+// The per-block counts: block b counts assignments [b CH, (b + 1) CH) per
+// expert into bcnt[b][0..n).
+__global__ __launch_bounds__(kPermWaves* kWave) void permute_count_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int n, int64_t CH, int32_t* __restrict__ bcnt) {
+    __shared__ int32_t cnt[kPermWaves][64];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int64_t b0 = (int64_t)blockIdx.x * CH, b1 = min(b0 + CH, A);
+    const int64_t per = ((b1 - b0 + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
+    const int64_t beg = min(b0 + (int64_t)w * per, b1);
+    cnt[w][lane] = count_segment(idx, beg, min(beg + per, b1), n, lane);
+    __syncthreads();
+    if (threadIdx.x < n) {
+        int32_t s = 0;
+        for (int ww = 0; ww < kPermWaves; ++ww) s += cnt[ww][threadIdx.x];
+        bcnt[(int64_t)blockIdx.x * n + threadIdx.x] = s;
+    }
+}
+
+// Passes over assignments [b0, b1): with bcnt (nblocks blocks of CH), the
+// block's bases come from the counts of the blocks before it; without, the
+// single workgroup covers everything.
+__global__ __launch_bounds__(kPermWaves* kWave) void permute_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int n, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ counts,
+    int64_t CH, const int32_t* __restrict__ bcnt, int nblocks) {
+    __shared__ int32_t cnt[kPermWaves][64];
+    __shared__ int32_t base[kPermWaves][64];
+    __shared__ int32_t before[64], total[64];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int64_t b0 = bcnt ? (int64_t)blockIdx.x * CH : 0;
+    const int64_t b1 = bcnt ? min(b0 + CH, A) : A;
+    // contiguous segment per wave, a multiple of 64 long
+    const int64_t per = ((b1 - b0 + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
+    const int64_t beg = min(b0 + (int64_t)w * per, b1);
+    const int64_t end = min(beg + per, b1);
+
+    cnt[w][lane] = count_segment(idx, beg, end, n, lane);
+    if (threadIdx.x < 64) {  // expert e: this block's base among all blocks
+        const int e = threadIdx.x;
+        int32_t bef = 0, tot = 0;
+        if (bcnt && e < n) {
+            for (int b = 0; b < nblocks; ++b) {
+                const int32_t c = bcnt[(int64_t)b * n + e];
+                if (b < (int)blockIdx.x) bef += c;
+                tot += c;
+            }
+        }
+        before[e] = bef;
+        total[e] = tot;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int32_t run = 0;
+        int32_t run = 0;  // first row of expert e (over all blocks)
         for (int e = 0; e < n; ++e) {
-            offsets[e] = run;
-            const int32_t start = run;
-            for (int ww = 0; ww < kPermWaves; ++ww) {
-                base[ww][e] = run;
-                run += cnt[ww][e];
+            int32_t blk = 0;  // this block's assignments of expert e
+            for (int ww = 0; ww < kPermWaves; ++ww) blk += cnt[ww][e];
+            const int32_t all = bcnt ? total[e] : blk;
+            if (blockIdx.x == 0) {
+                offsets[e] = run;
+                if (counts) counts[e] = all;
             }
-            if (counts) counts[e] = run - start;
+            int32_t r = run + before[e];
+            for (int ww = 0; ww < kPermWaves; ++ww) {
+                base[ww][e] = r;
+                r += cnt[ww][e];
+            }
+            run += all;
         }
-        offsets[n] = run;
+        if (blockIdx.x == 0) offsets[n] = run;
     }
     __syncthreads();
 
@@ -88,10 +145,26 @@ __global__ __launch_bounds__(kPermWaves* kWave) void permute_kernel(
 
 }  // namespace
 
+int permute_blocks(int64_t A) {
+    if (A < kPermSplitMin) return 1;
+    const int64_t ch = permute_chunk(A);
+    return (int)((A + ch - 1) / ch);
+}
+
 hipError_t launch_permute(const int32_t* idx, int64_t A, int n, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermWaves * kWave), 0, s, idx, A, n,
-                       offsets, perm, inv, counts);
+                          int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s,
+                          int32_t* scratch) {
+    const int nb = permute_blocks(A);
+    if (!scratch || nb <= 1) {
+        hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermWaves * kWave), 0, s, idx, A, n,
+                           offsets, perm, inv, counts, (int64_t)0, (const int32_t*)nullptr, 1);
+        return hipGetLastError();
+    }
+    const int64_t ch = permute_chunk(A);
+    hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nb), dim3(kPermWaves * kWave), 0, s,
+                       idx, A, n, ch, scratch);
+    hipLaunchKernelGGL(permute_kernel, dim3((unsigned)nb), dim3(kPermWaves * kWave), 0, s, idx,
+                       A, n, offsets, perm, inv, counts, ch, (const int32_t*)scratch, nb);
     return hipGetLastError();
 }
 

@@ -30,6 +30,15 @@ def test_bf16_ragged(path, T, d, d_ff):
     check_layer(L, 2, path=path, label=f"ragged-{path}")
 
 
+@pytest.mark.parametrize("T,n,K", [(2500, 8, 2), (1200, 64, 8)])
+def test_many_assignments_every_token(T, n, K):
+    # T K >= 4096 assignments: the permutation runs over several workgroups
+    # (per-block counts, then bases from the blocks before); every token is
+    # compared, so any misplaced row shows
+    L = small_layer(T, 128, 192, n, K, seed=T + n)
+    rep, _ = check_layer(L, K, label=f"many-assignments-{T}x{K}")
+
+
 @pytest.mark.parametrize("path", ["tiled", "skinny"])
 def test_fp32_ragged(path):
     L = small_layer(150, 136, 200, 8, 2, dtype="f32", seed=3)
