@@ -131,11 +131,13 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(
         }
         for (int j = 0; j < K; ++j) {
             const int pos = inv[t * K + j];
-            const float* src = DX + (int64_t)pos * d + k;
             const int np = pos >= R0 ? Sr : 1;
+            // partial q >= 1: row A + (q - 1)(A - R0) + pos - R0 (R0 = 0: q A + pos)
+            const int64_t A = split_stride / d;
 #pragma unroll 4
             for (int q = 0; q < np; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(src + q * split_stride);
+                const int64_t r = q == 0 ? pos : A + (int64_t)(q - 1) * (A - R0) + pos - R0;
+                const float4 v = *reinterpret_cast<const float4*>(DX + r * d + k);
                 s[0] += v.x;
                 s[1] += v.y;
                 s[2] += v.z;

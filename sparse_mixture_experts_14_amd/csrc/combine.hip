@@ -8,9 +8,10 @@
 // One thread per 4 output columns (a workgroup covers 1024 columns of one
 // token).  Each token gathers its K expert rows (fp32, possibly split into
 // partial sums of the down projection: S for every row, or, after the tiled
-// down projection, Sr for the rows from R0 on and one before) and sums them
-// in a fixed order -- partials in split order, then slots in k order -- so
-// the result is deterministic and no atomics are needed.  The sum is rounded once into the output dtype (RNE).
+// down projection, Sr for the rows from R0 on and one before; partial s >= 1
+// of row p at row A + (s - 1)(A - R0) + p - R0) and sums them in a fixed
+// order -- partials in split order, then slots in k order -- so the result
+// is deterministic and no atomics are needed.  The sum is rounded once into the output dtype (RNE).
 // The residual variant adds x_t (fp32) before that single rounding.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -25,7 +26,6 @@ __global__ __launch_bounds__(256) void combine_kernel(
     TOut* __restrict__ y, const int* __restrict__ split_meta) {
     const int cb = (d + 1023) / 1024;  // workgroups per token
     const int64_t t = blockIdx.x / cb;
-    const int64_t split_stride = A * (int64_t)d;
     const int c = (int)(blockIdx.x % cb) * 1024 + threadIdx.x * 4;
     // rows from R0 on hold Sr partial sums, the rows before it one
     const int R0 = split_meta ? split_meta[0] : 0;
@@ -38,8 +38,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
             const float* __restrict__ row = O + pos * (int64_t)d + c;
             float4 o = *reinterpret_cast<const float4*>(row);
             const int np = pos >= R0 ? Sr : 1;
+            // partial s >= 1: row A + (s - 1)(A - R0) + pos - R0 (R0 = 0: s A + pos)
+            const float* __restrict__ more = O + (A + pos - R0) * (int64_t)d + c;
             for (int s = 1; s < np; ++s) {
-                const float4 p = *reinterpret_cast<const float4*>(row + s * split_stride);
+                const float4 p = *reinterpret_cast<const float4*>(
+                    more + (int64_t)(s - 1) * (A - R0) * d);
                 o.x += p.x;
                 o.y += p.y;
                 o.z += p.z;

@@ -619,15 +619,18 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // This block's tile L among the tiles of rows [lo, hi), and its K split
     // ks of nsplit.
     int lo = offsets[0], hi = offsets[n], ks = 0, nsplit = splits, L = 0;
+    int64_t part0 = 0;  // first row of this block's partial-sum buffer, minus R0 (see below)
     if (cus > 0) {
         // Split only the remainder (the down projection): the tiles fill
         // tiles / cus whole rounds of the CUs, plus r = tiles % cus left over.
         // The last row tiles in expert order (at least r tiles, whole rows of
         // tiles, from row R0 on) run as Sr K splits each, Sr = cus / their
-        // count (at most `splits`), so they make one short round instead of
-        // a mostly idle full one; every other tile runs its whole K once.
-        // Rows >= R0 hold Sr partial sums, the rest one; (R0, Sr) go to
-        // split_meta for the combine.
+        // count at most, so they make one short round instead of a mostly
+        // idle full one; every other tile runs its whole K once.  Rows >= R0
+        // hold Sr partial sums, the rest one: buffer 0 holds every row's
+        // first ([A][N]), and split s >= 1 of row p >= R0 sits at row
+        // A + (s - 1)(A - R0) + p - R0.  (R0, Sr) go to split_meta for the
+        // combine.
         int R0 = offsets[n], Sr = 1, Trem = 0;
         const int r = tiles % cus;
         if (r > 0 && splits > 1) {
@@ -644,7 +647,14 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
                 Trem += take * ntn_s;
                 if (take > 0) R0 = s0 + (nsq_q - take) * SQ::BM;
             }
-            Sr = min(splits, cus / Trem);
+            // Partial sums past the first are stored for rows >= R0 only,
+            // (A - R0) rows per split, in the (splits - 1) A rows of buffers
+            // the workspace holds beyond buffer 0: that bounds Sr, as do the
+            // K steps (and 16, so each split keeps several).
+            const int64_t rows_rem = (int64_t)offsets[n] - R0;
+            const int64_t fit = 1 + (int64_t)(splits - 1) * offsets[n] / max((int64_t)1, rows_rem);
+            const int nk = (Kdim + BK - 1) / BK;
+            Sr = (int)min((int64_t)min(min(cus / Trem, nk), 16), fit);
             if (Sr < 2) {
                 Sr = 1;
                 R0 = offsets[n];
@@ -672,6 +682,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
             L = u - ks * Trem;
             lo = R0;
             nsplit = Sr;
+            // split ks >= 1 writes row p to row A + (ks - 1)(A - R0) + p - R0
+            if (ks > 0)
+                part0 = (int64_t)offsets[n] + (int64_t)(ks - 1) * (offsets[n] - R0) - R0;
         }
     } else {
         const int per_xcd = (tiles * splits + 7) / 8;
@@ -680,6 +693,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
         if (jx >= per_xcd || L0 >= tiles * splits) return;
         ks = L0 / tiles;  // K split of this block
         L = L0 - ks * tiles;
+        part0 = split_stride / N * ks;  // buffer ks: rows A ks ..
     }
     // the expert of tile L, over the rows of [lo, hi) (R0 is a row-tile
     // boundary of its expert, so both sides keep the expert's own tiling)
@@ -720,7 +734,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     }
     t.Kdim = Kdim;
     t.N = N;
-    t.Cout = static_cast<uint8_t*>(Cout) + ks * split_stride * (GATEUP || EPI == 2 ? 2 : 4);
+    t.Cout = static_cast<uint8_t*>(Cout) + part0 * N * (GATEUP || EPI == 2 ? 2 : 4);
     t.Cout2 = Cout2;
     const int nk_all = (Kdim + BK - 1) / BK;
     const int per_split = (nk_all + nsplit - 1) / nsplit;
