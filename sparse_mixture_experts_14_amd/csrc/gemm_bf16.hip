@@ -595,7 +595,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // of tiles and the 32 tiles its CUs run together are neighbours in the
     // order below, sharing token and weight tiles in its L2.
     //
-    // Order: split, expert, row group (GM square row tiles; the wide row tile
+    // Order: (split,) expert, row group (GM square row tiles; the wide row tile
     // joins the last group), column pair, then inside a column pair the
     // group's square tiles of both columns followed by the wide tile that
     // spans them -- all tiles reading one weight panel run back to back.
@@ -619,7 +619,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t A_src_rows,
     // This block's tile L among the tiles of rows [lo, hi), and its K split
     // ks of nsplit.
     int lo = offsets[0], hi = offsets[n], ks = 0, nsplit = splits, L = 0;
-    int64_t part0 = 0;  // first row of this block's partial-sum buffer, minus R0 (see below)
+    int64_t part0 = 0;  // this block writes output row p at row part0 + p of Cout
     if (cus > 0) {
         // Split only the remainder (the down projection): the tiles fill
         // tiles / cus whole rounds of the CUs, plus r = tiles % cus left over.
