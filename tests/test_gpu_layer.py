@@ -30,6 +30,14 @@ def test_bf16_ragged(path, T, d, d_ff):
     check_layer(L, 2, path=path, label=f"ragged-{path}")
 
 
+def test_down_projection_split_rows_every_token():
+    # d = 4096 gives the down projection 16 column tiles, so 2200 tokens make
+    # a few more tiles than one round of 256 CUs: whole-K tiles below R0,
+    # K-split tiles (packed partial sums) from R0 on; every token compared
+    L = small_layer(2200, 4096, 128, 8, 2, seed=77)
+    check_layer(L, 2, path="tiled", label="down-split-rows")
+
+
 @pytest.mark.parametrize("T,n,K", [(2500, 8, 2), (1200, 64, 8)])
 def test_many_assignments_every_token(T, n, K):
     # T K >= 4096 assignments: the permutation runs over several workgroups
