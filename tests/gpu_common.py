@@ -45,9 +45,12 @@ def host_inputs(L: dict) -> dict:
 
 def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows=None,
                 path: str | None = None, label: str = "", tol: float | None = None,
-                host: dict | None = None):
-    """Run the GPU layer on the device tensors in L, compare with the oracle.
-    Returns (report dict, y_gpu tensor)."""
+                host: dict | None = None, row_tol: float | None = None):
+    """Run the GPU layer on the device tensors in L, compare with the oracle:
+    the whole compared output against tol, and every compared row's own
+    error (|dy_row| over max(|y_row|, the median row norm)) against row_tol,
+    so that one misplaced row fails even among a million.  Returns (report
+    dict, y_gpu tensor)."""
     x = L["x"]
     T = x.shape[0]
     n = L["Wg"].shape[1]
@@ -87,6 +90,13 @@ def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows
     say(f"       rel_l2={err:.3e} max_abs={rep['max_abs']:.3e} near_ties={rep['near_ties']} "
         f"alt={nalt} gate_err={rep['gate_max_abs_err']:.2e} tol={tol}")
     assert err <= tol, f"rel L2 {err} > {tol}"
+    row_tol = row_tol if row_tol is not None else P.row_tol_for(x.dtype)
+    if len(rows):
+        per_row = P.row_errors(yg, yref)
+        worst = int(np.argmax(per_row))
+        rep["row_err"] = float(per_row[worst])
+        say(f"       worst row {rows[worst]}: error {per_row[worst]:.3e} (row_tol {row_tol})")
+        assert per_row[worst] <= row_tol, f"row {rows[worst]}: error {per_row[worst]} > {row_tol}"
     return rep, y
 
 

@@ -26,10 +26,28 @@ import torch
 TAU = 1e-3
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
+# Bound on each row's own error, |y_gpu - y_ref| over max(|y_ref|, median row
+# norm): a few times the whole-output bound, far below the ~1 that a row
+# computed from the wrong token or expert gives.
+ROW_TOL_BF16 = 5e-2
+ROW_TOL_F32 = 1e-4
 
 
 def tol_for(dtype) -> float:
     return TOL_F32 if dtype == torch.float32 else TOL_BF16
+
+
+def row_tol_for(dtype) -> float:
+    return ROW_TOL_F32 if dtype == torch.float32 else ROW_TOL_BF16
+
+
+def row_errors(y_gpu, y_ref) -> np.ndarray:
+    """Per-row error |y_gpu - y_ref| / max(|y_ref|, median row norm)."""
+    a = np.asarray(y_gpu, dtype=np.float64)
+    b = np.asarray(y_ref, dtype=np.float64)
+    rn = np.linalg.norm(b, axis=1)
+    floor = max(float(np.median(rn)), 1e-300) if rn.size else 1.0
+    return np.linalg.norm(a - b, axis=1) / np.maximum(rn, floor)
 
 
 def valid_sets(logits_row: np.ndarray, K: int, tau: float = TAU):

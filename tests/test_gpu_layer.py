@@ -38,11 +38,14 @@ def test_down_projection_split_rows_every_token():
     check_layer(L, 2, path="tiled", label="down-split-rows")
 
 
-@pytest.mark.parametrize("T,n,K", [(2500, 8, 2), (1200, 64, 8)])
+@pytest.mark.parametrize("T,n,K", [(2500, 8, 2), (1200, 64, 8), (524000, 8, 2),
+                                   (131000, 64, 8)])
 def test_many_assignments_every_token(T, n, K):
     # T K >= 4096 assignments: the permutation runs over several workgroups
-    # (per-block counts, then bases from the blocks before); every token is
-    # compared, so any misplaced row shows
+    # (per-block counts, then bases from the blocks before).  1,048,000
+    # assignments take the most blocks, 1024 of 1024 (the last one ragged).
+    # Every token is compared, each row against its own bound, so any
+    # misplaced row shows.
     L = small_layer(T, 128, 192, n, K, seed=T + n)
     rep, _ = check_layer(L, K, label=f"many-assignments-{T}x{K}")
 

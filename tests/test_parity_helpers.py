@@ -32,3 +32,19 @@ def test_rel_l2():
     a = np.ones((3, 4))
     assert P.rel_l2(a, a) == 0.0
     assert abs(P.rel_l2(a * 1.01, a) - 0.01) < 1e-12
+
+
+def test_row_errors_catch_one_misplaced_row_among_many():
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((100000, 64))
+    got = ref * (1 + 2.0**-8 * rng.standard_normal(ref.shape))  # bf16-sized noise
+    assert P.rel_l2(got, ref) < P.TOL_BF16
+    assert P.row_errors(got, ref).max() < P.ROW_TOL_BF16
+    got[[17, 18]] = got[[18, 17]]  # two tokens' rows swapped
+    assert P.rel_l2(got, ref) < P.TOL_BF16  # the whole-output bound misses it
+    err = P.row_errors(got, ref)
+    assert err[17] > 10 * P.ROW_TOL_BF16 and err[18] > 10 * P.ROW_TOL_BF16
+    # a row whose own norm is tiny is measured against the median row norm
+    ref[3] *= 1e-6
+    got[3] = ref[3] + 1e-9
+    assert P.row_errors(got, ref)[3] < 1e-6
