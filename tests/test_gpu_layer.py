@@ -133,3 +133,16 @@ def test_deterministic_and_permutation_equivariant(path):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(yp, y1[p])
+
+
+@pytest.mark.parametrize("T,d,K", [(1, 4096, 2), (16, 2048, 2), (32, 4096, 8), (7, 4096, 1),
+                                   (33, 4096, 2)])
+def test_few_tokens_route_like_the_router(T, d, K):
+    # the layer's routing (bf16, n = 8, the router's resident-weight widths)
+    # gives the same experts and gates, bit for bit, as the standalone
+    # router, and every token's output matches the oracle
+    L = small_layer(T, d, 256, 8, K, seed=T * 7 + K)
+    check_layer(L, K, label=f"few-tokens-T{T}-d{d}-K{K}")
+    _, idx, gate, _ = moe.forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], K)
+    ridx, rgate = moe.route(L["x"], L["Wg"], K)
+    assert torch.equal(idx, ridx) and torch.equal(gate, rgate)
