@@ -25,6 +25,10 @@ MUTANTS = {
     "gate_dropped": ("y[c] += g[j] * o[c];", "y[c] += o[c];"),
     "expert_stride": ("W1 + e * d_ff * d, W3 + e * d_ff * d", "W1 + e * d_ff, W3 + e * d_ff"),
     "rms_mean": ("ss / (double)d + eps", "ss + eps"),
+    "rms_eps_outside_sqrt": ("const double inv = 1.0 / sqrt(ss / (double)d + eps);",
+                             "const double inv = 1.0 / (sqrt(ss / (double)d) + eps);"),
+    "rms_eps_dropped": ("const double inv = 1.0 / sqrt(ss / (double)d + eps);",
+                        "const double inv = 1.0 / sqrt(ss / (double)d);"),
     "residual_dropped": ("yr[k] += (double)xt[k];", "yr[k] += 0.0;"),
     "second_slot_gate": ("for (int32_t j = 0; j < K; ++j) g[j] /= z;",
                          "for (int32_t j = 0; j < K; ++j) g[j] /= (j ? z : 1.0);"),
@@ -75,6 +79,8 @@ BACKWARD_MUTANTS.update({
                                "dx[r * d + k] = 0.0 * (double)dy[t * d + k] + sc"),
     "block_scale_missing": ("sc * (du[r * d + k] - u[k] * c / (double)d)",
                             "(du[r * d + k] - u[k] * c / (double)d)"),
+    "block_eps_outside_sqrt": ("const double sc = 1.0 / sqrt(ss / (double)d + eps);",
+                               "const double sc = 1.0 / (sqrt(ss / (double)d) + eps);"),
 })
 
 BACKWARD_PINS = [
