@@ -30,6 +30,13 @@ MUTANTS = {
     "rms_eps_dropped": ("const double inv = 1.0 / sqrt(ss / (double)d + eps);",
                         "const double inv = 1.0 / sqrt(ss / (double)d);"),
     "residual_dropped": ("yr[k] += (double)xt[k];", "yr[k] += 0.0;"),
+    "softmax_before_topk": (
+        "    masked_softmax(l, sel, K, g);\n    for (int64_t c = 0; c < d; ++c) y[c] = 0.0;",
+        "    {\n        double m0 = l[0], z0 = 0.0;\n"
+        "        for (int32_t i = 1; i < n; ++i) if (l[i] > m0) m0 = l[i];\n"
+        "        for (int32_t i = 0; i < n; ++i) z0 += exp(l[i] - m0);\n"
+        "        for (int32_t j = 0; j < K; ++j) g[j] = exp(l[sel[j]] - m0) / z0;\n"
+        "    }\n    for (int64_t c = 0; c < d; ++c) y[c] = 0.0;"),
     "second_slot_gate": ("for (int32_t j = 0; j < K; ++j) g[j] /= z;",
                          "for (int32_t j = 0; j < K; ++j) g[j] /= (j ? z : 1.0);"),
 }
