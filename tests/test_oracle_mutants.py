@@ -1,6 +1,7 @@
 """The pins must be able to fail: plant plausible mistakes in a copy of the
 oracle's C source (on the CPU, in a temporary directory), build the mutant, and
-check that at least one pin in tests/test_oracle_pins.py rejects it."""
+check that at least one pin (tests/test_oracle_pins.py, test_oracle_backward.py,
+test_oracle_forced.py) rejects it."""
 import os
 import subprocess
 
@@ -8,6 +9,7 @@ import pytest
 
 import oracle as oracle_pkg
 from tests import test_oracle_backward as bpins
+from tests import test_oracle_forced as fpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
@@ -39,6 +41,16 @@ MUTANTS = {
         "    }\n    for (int64_t c = 0; c < d; ++c) y[c] = 0.0;"),
     "second_slot_gate": ("for (int32_t j = 0; j < K; ++j) g[j] /= z;",
                          "for (int32_t j = 0; j < K; ++j) g[j] /= (j ? z : 1.0);"),
+    # the caller's expert set ignored (TopK's own choice used instead), at
+    # every forced-routing site
+    "forced_ignored": ("if (forced) {", "if (forced && 0) {"),
+    # the caller's set taken, but sorted back into logit order
+    "forced_reordered": ("for (int32_t j = 0; j < K; ++j) sel[j] = forced[j];",
+                         "for (int32_t j = 0; j < K; ++j) sel[j] = forced[j];\n"
+                         "        for (int32_t j = 1; j < K; ++j)\n"
+                         "            for (int32_t q = j; q > 0 && l[sel[q]] > l[sel[q - 1]]; --q) {\n"
+                         "                int32_t tmp = sel[q]; sel[q] = sel[q - 1]; sel[q - 1] = tmp;\n"
+                         "            }"),
 }
 
 PIN_TESTS = [
@@ -53,6 +65,9 @@ PIN_TESTS = [
     lambda o: pins.test_zero_token(o),
     lambda o: pins.test_duplicate_router_columns_tie_to_lower_index(o),
     lambda o: pins.test_block_layer_is_residual_over_rmsnorm(o),
+    lambda o: fpins.test_forced_forward_takes_the_given_set(None),
+    lambda o: fpins.test_forced_forward_takes_the_given_set(1e-5),
+    lambda o: fpins.test_forced_rows_subset_and_three_slots(),
 ]
 
 
@@ -90,6 +105,13 @@ BACKWARD_MUTANTS.update({
                                "const double sc = 1.0 / (sqrt(ss / (double)d) + eps);"),
 })
 
+# The forced-routing sites of the backward (token_backward) and of the entry
+# path (entries_impl), one at a time: (old, new, which occurrence).
+BACKWARD_MUTANTS.update({
+    "bwd_forced_ignored": ("if (forced) {", "if (forced && 0) {", 1),
+    "entries_forced_ignored": ("if (forced) {", "if (forced && 0) {", 2),
+})
+
 BACKWARD_PINS = [
     lambda o: bpins.test_block_backward_matches_finite_differences(),
     lambda o: bpins.test_block_backward_dense_mixture_autograd(),
@@ -101,13 +123,28 @@ BACKWARD_PINS = [
     lambda o: bpins.test_single_expert_backward_is_swiglu_autograd(),
     lambda o: bpins.test_dense_mixture_backward_when_K_equals_n(),
     lambda o: bpins.test_router_gradient_rows_sum_to_zero(),
+    lambda o: fpins.test_forced_backward_matches_autograd(None),
+    lambda o: fpins.test_forced_backward_matches_autograd(1e-5),
+    lambda o: fpins.test_forced_backward_entries_match_autograd(None),
+    lambda o: fpins.test_forced_backward_entries_match_autograd(1e-5),
 ]
 
 
-def _build_mutant(old, new, tmp_path, monkeypatch):
-    src = open(SRC).read()
+def _mutate(src, old, new, nth=None):
+    """src with old replaced by new: every occurrence, or only the nth
+    (0-based) when nth is given."""
     assert src.count(old) >= 1, f"mutation site not found: {old!r}"
-    mutated = src.replace(old, new)
+    if nth is None:
+        return src.replace(old, new)
+    parts = src.split(old)
+    assert len(parts) > nth + 1, f"occurrence {nth} of {old!r} not found"
+    return old.join(parts[:nth + 1]) + new + old.join(parts[nth + 1:])
+
+
+def _build_mutant(site, tmp_path, monkeypatch):
+    """Compile the oracle with one planted mistake; site = (old, new) or
+    (old, new, nth)."""
+    mutated = _mutate(open(SRC).read(), *site)
     c_path = tmp_path / "mutant.c"
     so_path = tmp_path / "libmutant.so"
     c_path.write_text(mutated)
@@ -119,7 +156,7 @@ def _build_mutant(old, new, tmp_path, monkeypatch):
 
 @pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
 def test_backward_mutant_is_caught(name, tmp_path, monkeypatch):
-    _build_mutant(*BACKWARD_MUTANTS[name], tmp_path, monkeypatch)
+    _build_mutant(BACKWARD_MUTANTS[name], tmp_path, monkeypatch)
     caught = 0
     for pin in BACKWARD_PINS:
         try:
@@ -132,17 +169,7 @@ def test_backward_mutant_is_caught(name, tmp_path, monkeypatch):
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, tmp_path, monkeypatch):
-    old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) >= 1, f"mutation site of {name} not found"
-    mutated = src.replace(old, new)
-    c_path = tmp_path / "mutant.c"
-    so_path = tmp_path / "libmutant.so"
-    c_path.write_text(mutated)
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o",
-                    str(so_path), str(c_path), "-lm"], check=True)
-    monkeypatch.setattr(oracle_pkg, "_LIB_PATH", str(so_path))
-    monkeypatch.setattr(oracle_pkg, "_lib", None)
+    _build_mutant(MUTANTS[name], tmp_path, monkeypatch)
     caught = 0
     for pin in PIN_TESTS:
         try:
