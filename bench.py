@@ -3,12 +3,16 @@
 MI355X, with the roofline of its dominant kernel and the fp64 oracle's CPU
 throughput beside it.
 
-One step = one call of the whole layer (router, permutation, gate/up GEMM,
-down GEMM, combine) on the workload's synthetic batch, inputs resident in HBM.
-Default workload: decode (T = 16 tokens, d = 4096, d_ff = 14336, n = 8, K = 2,
-bf16), bound by reading the touched experts' weights.  Prints one JSON line.
+One step = one pass of the whole layer (router, permutation, gate/up GEMM,
+down GEMM, combine) over the workload's synthetic batch, inputs resident in
+HBM.  Default workload: the stack, 32 independent layers
+y = x + MoE(RMSNorm(x)) at Mixtral shape (T = 2048 tokens, d = 4096,
+d_ff = 14336, n = 8, K = 2, bf16, 90 GB of expert weights resident), the
+largest configuration; one step carries the tokens through all 32 layers.
+The other workloads (decode T = 16, prefill T = 4096, skewed routing
+T = 16384, tiny fp32) are selected with --workload.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skew|stack|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload stack|decode|prefill|skew|tiny]
 """
 from __future__ import annotations
 
@@ -106,6 +110,18 @@ def algorithmic_work(w, counts):
     return {"touched_experts": touched, "bytes": wbytes + act, "flops": flops}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, L, budget_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload's
     tokens (timing each oracle call; repeats until ~budget_s)."""
@@ -139,7 +155,7 @@ def cpu_baseline(w, L, budget_s: float):
         sample = f"{tokens} tokens drawn from the workload's {w.T} ({reps} oracle call(s))"
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model()}
 
 
 def traffic_for(workload: str, src_sha: str):
@@ -267,7 +283,7 @@ def backward_cpu_baseline(w, L, dy, budget_s: float, train: bool = False, eps=No
             "kind": "oracle",
             "sample": f"{'forward and backward' if train else 'backward'} of the "
                       f"workload's first {m} tokens (x, dy rows; every gradient) x{reps}",
-            "seconds": round(elapsed, 2), "cpu": platform.processor() or platform.machine()}
+            "seconds": round(elapsed, 2), "cpu": cpu_model()}
 
 
 def bench_backward(args, w, dev, train=False):
@@ -398,7 +414,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode",
+    ap.add_argument("--workload", default="stack",
                     choices=["tiny", "decode", "prefill", "skew", "stack"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -435,6 +451,7 @@ def main():
 
     import sparse_mixture_experts_14_amd as moe
     from sparse_mixture_experts_14_amd import workloads as W
+    from sparse_mixture_experts_14_amd.stack import Stack
 
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -451,24 +468,17 @@ def main():
         L = W.make_layer(w, device=dev)
         layers = [L]
         x0 = L["x"]
-    lay = moe.Layer(w.T, w.d, w.d_ff, w.n, w.K, w.torch_dtype, dev)
-    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    chain = Stack(layers, w.T, w.d, w.d_ff, w.n, w.K, w.torch_dtype, dev, eps=w.eps)
+    lay = chain.lay
 
     def step(stage_ev=None):
-        x = x0
-        for i, P in enumerate(layers):
-            y = bufs[i % 2]
+        def before(i):
             if stage_ev is not None:
                 moe._lib.set_stage_events_raw("gate_up", stage_ev[i][0].handle.value,
                                               stage_ev[i][1].handle.value)
             else:
                 moe._lib.set_stage_events_raw("gate_up")
-            if w.eps is not None:
-                lay.block_forward(x, P["Wg"], P["W1"], P["W3"], P["W2"], w.eps, out=y)
-            else:
-                lay.forward(x, P["Wg"], P["W1"], P["W3"], P["W2"], out=y)
-            x = y
-        return x
+        return chain.run(x0, before=before)
 
     for _ in range(args.warmup):
         step()

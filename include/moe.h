@@ -101,9 +101,11 @@ moe_status_t moe_route(const void* x, const void* w_g, int64_t T, int64_t d,
                        int32_t n, int32_t K, moe_dtype_t dt, int32_t* idx,
                        float* gate, void* stream);
 
-/* Token permutation ("experts with zero gate need not be computed": each
- * expert gets the contiguous list of the assignments routed to it).  Input
- * idx[T][K]; assignment a = t*K + k goes to expert idx[a].  Output:
+/* Token permutation.  Only the K experts a token keeps have a non-zero gate,
+ * so only they need to run for it (GeekNews summary, section "Cara Komputasi
+ * Layer MoE"); each expert therefore gets the contiguous list of the
+ * assignments routed to it.
+ * Input idx[T][K]; assignment a = t*K + k goes to expert idx[a].  Output:
  *   offsets[n+1]  offsets[e] = first position of expert e, offsets[n] = T*K
  *   perm[T*K]     perm[pos] = a, positions of one expert in increasing a
  *                 (a stable counting sort by expert)
@@ -257,6 +259,21 @@ moe_status_t moe_block_backward_saved(const void* x, const void* w_g, const void
  * must stay valid while set; NULL, NULL clears the hook.  Returns
  * MOE_ERR_INVALID_ARGUMENT for an unknown stage or a single NULL. */
 moe_status_t moe_set_stage_events(int32_t stage, void* start_event, void* end_event);
+
+/* bf16 GEMM kernel families (moe_set_gemm_path). */
+typedef enum moe_gemm_path {
+    MOE_GEMM_AUTO = 0,   /* chosen from the sizes: weight stream for few rows per expert */
+    MOE_GEMM_TILED = 1,  /* MFMA tiles over many rows per expert */
+    MOE_GEMM_STREAM = 2  /* weight stream (when its tables fit; tiled otherwise) */
+} moe_gemm_path_t;
+
+/* Testing and tuning hook (not part of the layer): later calls made by this
+ * thread use the given bf16 GEMM kernel family instead of the one chosen from
+ * the sizes.  Both families compute the same layer; the hook exists so that
+ * tests can run each on the same input.  MOE_GEMM_AUTO restores the default.
+ * The workspace bound (moe_workspace_bytes) covers every choice.  Returns
+ * MOE_ERR_INVALID_ARGUMENT for an unknown value. */
+moe_status_t moe_set_gemm_path(int32_t path);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t status);

@@ -22,12 +22,16 @@ MOE_ERR_WORKSPACE_TOO_SMALL = 3
 MOE_ERR_HIP = 4
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_GEMM_AUTO = 0
+MOE_GEMM_TILED = 1
+MOE_GEMM_STREAM = 2
 
 EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_forward", "moe_block_forward", "moe_set_stage_events", "moe_status_string",
            "moe_last_error", "moe_backward", "moe_backward_workspace_bytes",
            "moe_saved_bytes", "moe_forward_train", "moe_backward_saved",
-           "moe_block_backward", "moe_block_forward_train", "moe_block_backward_saved")
+           "moe_block_backward", "moe_block_forward_train", "moe_block_backward_saved",
+           "moe_set_gemm_path")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
           "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
@@ -69,6 +73,8 @@ def load(path: str | None = None):
                                 V, V, V, V]
     lib.moe_set_stage_events.restype = ctypes.c_int
     lib.moe_set_stage_events.argtypes = [I32, V, V]
+    lib.moe_set_gemm_path.restype = ctypes.c_int
+    lib.moe_set_gemm_path.argtypes = [I32]
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, F,
                                       V, V, SZ, V, V, V, V]
@@ -133,6 +139,16 @@ def set_stage_events_raw(stage: str, start: int | None = None, end: int | None =
     """Record the hipEvent_t handles (start, end) around `stage` in later layer
     calls on this thread; no handles clears the hook."""
     _check(load().moe_set_stage_events(STAGES[stage], start, end), "moe_set_stage_events")
+
+
+GEMM_PATHS = {None: MOE_GEMM_AUTO, "auto": MOE_GEMM_AUTO, "tiled": MOE_GEMM_TILED,
+              "skinny": MOE_GEMM_STREAM, "stream": MOE_GEMM_STREAM}
+
+
+def set_gemm_path(path: str | None):
+    """Testing hook: later layer calls on this thread use the named bf16 GEMM
+    family ("tiled", "stream"/"skinny"; None or "auto" = chosen by size)."""
+    _check(load().moe_set_gemm_path(GEMM_PATHS[path]), "moe_set_gemm_path")
 
 
 def workspace_bytes(T: int, d: int, d_ff: int, n: int, K: int, dtype: torch.dtype) -> int:

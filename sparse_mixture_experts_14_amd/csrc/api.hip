@@ -7,6 +7,7 @@
 // Arguments are checked before anything is enqueued; see include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -46,26 +47,28 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Which GEMM kernels run for these sizes, and how many K splits the down
-// projection uses.  Depends on sizes only (so the workspace bound holds); the
-// environment variable MOE_GEMM_PATH=tiled|skinny forces a bf16 path (a
-// testing and tuning knob).
+// projection uses.  Depends on sizes only (so the workspace bound holds);
+// moe_set_gemm_path (a per-thread testing and tuning hook) can force a bf16
+// path.
+thread_local int32_t g_gemm_path = MOE_GEMM_AUTO;
 // Upper bound of the K splits of the down projection (partial sums in the
 // workspace): up to 8 for the skinny kernel (few rows), 4 for the tiled one.
 int requested_down_splits(int64_t T, int32_t K) { return T * K <= 256 ? 8 : 4; }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; threads that
+// race on the first query store the same value).
 int device_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int cus = 0;
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                 hipSuccess || cus <= 0)
             cus = 256;
-        cache[dev] = cus;
+        cache[dev].store(cus, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return cus;
 }
 
 // Waves per CU and K splits of a skinny GEMM: the pair whose item count
@@ -106,10 +109,8 @@ Plan choose_plan(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_d
     const int64_t A = T * K;
     // expected rows per expert; the skinny kernel re-streams weights per 16 rows
     p.skinny = A <= 16 * (int64_t)n;
-    if (const char* f = getenv("MOE_GEMM_PATH")) {
-        if (!strcmp(f, "tiled")) p.skinny = false;
-        if (!strcmp(f, "skinny")) p.skinny = true;
-    }
+    if (g_gemm_path == MOE_GEMM_TILED) p.skinny = false;
+    if (g_gemm_path == MOE_GEMM_STREAM) p.skinny = true;
     if (!moe::skinny_fits(T, A, d, d_ff, 1) ||
         !moe::skinny_fits(A, A, d_ff, d, requested_down_splits(T, K)))
         p.skinny = false;
@@ -713,6 +714,13 @@ moe_status_t moe_set_stage_events(int32_t stage, void* start_event, void* end_ev
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_set_stage_events: give both events or none");
     g_ev_start[stage] = static_cast<hipEvent_t>(start_event);
     g_ev_end[stage] = static_cast<hipEvent_t>(end_event);
+    return MOE_OK;
+}
+
+moe_status_t moe_set_gemm_path(int32_t path) {
+    if (path < MOE_GEMM_AUTO || path > MOE_GEMM_STREAM)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_set_gemm_path: path %d", path);
+    g_gemm_path = path;
     return MOE_OK;
 }
 

@@ -2,7 +2,6 @@
 through the C ABI, run the oracle, compare."""
 from __future__ import annotations
 
-import os
 import sys
 
 import numpy as np
@@ -20,23 +19,17 @@ def say(*a):
 
 
 class forced_path:
-    """Select the bf16 GEMM kernels (tiled / skinny) for the calls inside."""
+    """Select the bf16 GEMM kernels (tiled / skinny) for the calls inside
+    (moe_set_gemm_path, a per-thread hook of the library)."""
 
     def __init__(self, path: str | None):
         self.path = path
 
     def __enter__(self):
-        self.old = os.environ.get("MOE_GEMM_PATH")
-        if self.path:
-            os.environ["MOE_GEMM_PATH"] = self.path
-        elif "MOE_GEMM_PATH" in os.environ:
-            del os.environ["MOE_GEMM_PATH"]
+        moe._lib.set_gemm_path(self.path)
 
     def __exit__(self, *exc):
-        if self.old is None:
-            os.environ.pop("MOE_GEMM_PATH", None)
-        else:
-            os.environ["MOE_GEMM_PATH"] = self.old
+        moe._lib.set_gemm_path(None)
 
 
 def host_inputs(L: dict) -> dict:
@@ -46,11 +39,8 @@ def host_inputs(L: dict) -> dict:
 def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows=None,
                 path: str | None = None, label: str = "", tol: float | None = None,
                 host: dict | None = None, row_tol: float | None = None):
-    """Run the GPU layer on the device tensors in L, compare with the oracle:
-    the whole compared output against tol, and every compared row's own
-    error (|dy_row| over max(|y_row|, the median row norm)) against row_tol,
-    so that one misplaced row fails even among a million.  Returns (report
-    dict, y_gpu tensor)."""
+    """Run the GPU layer on the device tensors in L, compare with the oracle
+    (compare_layer).  Returns (report dict, y_gpu tensor)."""
     x = L["x"]
     T = x.shape[0]
     n = L["Wg"].shape[1]
@@ -64,6 +54,22 @@ def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows
             y, idx, gate, counts = moe.forward(x, L["Wg"], L["W1"], L["W3"], L["W2"], K)
         torch.cuda.synchronize()
     H = host if host is not None else host_inputs(L)
+    rep = compare_layer(H, K, idx, gate, counts, y, rows=rows, block=block, eps=eps, tol=tol,
+                        row_tol=row_tol, dtype=x.dtype)
+    return rep, y
+
+
+def compare_layer(H: dict, K: int, idx, gate, counts, y, *, rows=None, block: bool = False,
+                  eps: float = 1e-5, tol: float | None = None, row_tol: float | None = None,
+                  dtype=torch.bfloat16) -> dict:
+    """Compare one GPU layer call with the oracle on the host inputs H:
+    routing on every token (parity.routing_report), counts_out, and the
+    outputs of the tokens ``rows`` (all when None) -- the whole compared
+    output against tol, and every compared row's own error (|dy_row| over
+    max(|y_row|, the median row norm)) against row_tol, so that one misplaced
+    row fails even among a million."""
+    T = H["x"].shape[0]
+    n = H["Wg"].shape[1]
     gi, gg, gc = P.to_np(idx), P.to_np(gate), P.to_np(counts)
     if block:
         lg, oi, og = oracle.block_route(H["x"], H["Wg"], K, eps)
@@ -85,19 +91,21 @@ def check_layer(L: dict, K: int, *, block: bool = False, eps: float = 1e-5, rows
     yref, nalt = P.expected_outputs(ofn, rows, gi[rows], K)
     yg = P.to_np(y)[rows]
     err = P.rel_l2(yg, yref)
-    rep.update(rel_l2=err, alt=nalt, max_abs=float(np.max(np.abs(yg - yref))) if len(rows) else 0.0)
-    tol = tol if tol is not None else P.tol_for(x.dtype)
-    say(f"       rel_l2={err:.3e} max_abs={rep['max_abs']:.3e} near_ties={rep['near_ties']} "
-        f"alt={nalt} gate_err={rep['gate_max_abs_err']:.2e} tol={tol}")
+    rep.update(rel_l2=err, alt=nalt, max_abs=float(np.max(np.abs(yg - yref))) if len(rows) else 0.0,
+               rows=len(rows))
+    tol = tol if tol is not None else P.tol_for(dtype)
+    say(f"       rows={len(rows)} rel_l2={err:.3e} max_abs={rep['max_abs']:.3e} "
+        f"near_ties={rep['near_ties']} alt={nalt} gate_err={rep['gate_max_abs_err']:.2e} "
+        f"tol={tol}")
     assert err <= tol, f"rel L2 {err} > {tol}"
-    row_tol = row_tol if row_tol is not None else P.row_tol_for(x.dtype)
+    row_tol = row_tol if row_tol is not None else P.row_tol_for(dtype)
     if len(rows):
         per_row = P.row_errors(yg, yref)
         worst = int(np.argmax(per_row))
         rep["row_err"] = float(per_row[worst])
         say(f"       worst row {rows[worst]}: error {per_row[worst]:.3e} (row_tol {row_tol})")
         assert per_row[worst] <= row_tol, f"row {rows[worst]}: error {per_row[worst]} > {row_tol}"
-    return rep, y
+    return rep
 
 
 def small_layer(T, d, d_ff, n, K, dtype="bf16", seed=0):

@@ -213,3 +213,18 @@ def test_block_backward_and_training_pair_validation(lib):
     assert lib.moe_block_forward_train(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d,
                                        d_ff, n, K, B.MOE_BF16, 1e-5, FAKE * 64, sv, sb - 1, ws,
                                        1 << 30, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_gemm_path_hook(lib):
+    """moe_set_gemm_path: the header's enum values are the binding's, unknown
+    values are rejected, and the default is restored with MOE_GEMM_AUTO."""
+    src = open(HEADER).read()
+    for name in ("MOE_GEMM_AUTO", "MOE_GEMM_TILED", "MOE_GEMM_STREAM"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == getattr(B, name), name
+    assert lib.moe_set_gemm_path(3) == B.MOE_ERR_INVALID_ARGUMENT
+    assert b"path 3" in lib.moe_last_error()
+    assert lib.moe_set_gemm_path(-1) == B.MOE_ERR_INVALID_ARGUMENT
+    for p in (B.MOE_GEMM_TILED, B.MOE_GEMM_STREAM, B.MOE_GEMM_AUTO):
+        assert lib.moe_set_gemm_path(p) == B.MOE_OK
+
