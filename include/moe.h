@@ -133,6 +133,24 @@ moe_status_t moe_forward(const void* x, const void* w_g, const void* w1,
                          int32_t* idx_out, float* gate_out, int32_t* counts_out,
                          void* stream);
 
+/* moe_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The layer's scratch lives in a static device array of
+ * the library, 64 MiB per device (held from the first call on a device until
+ * the process ends): enough for T <= 256 tokens at d = 4096, d_ff = 14336,
+ * n = 8, K = 2.  Larger sizes (moe_workspace_bytes(...) > 64 MiB) return
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  No device memory is
+ * allocated or freed.  All calls on one device share that device's array, so
+ * calls that may overlap in time on one device (different streams, or
+ * different host threads) race and give undefined results; serialise them,
+ * e.g. on one stream.  Same arguments, outputs and rules as moe_forward
+ * otherwise; y is bitwise equal to moe_forward's. */
+moe_status_t moe_forward_noalloc(const void* x, const void* w_g, const void* w1,
+                                 const void* w3, const void* w2, int64_t T, int64_t d,
+                                 int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
+                                 void* y, int32_t* idx_out, float* gate_out,
+                                 int32_t* counts_out, void* stream);
+
 /* One layer of a pre-normalised residual stack (the MoE replaces every
  * feed-forward sub-block, "Core ideas" of the xyznot digest; the
  * normalisation and residual are this workload's definition, not the

@@ -31,7 +31,7 @@ EXPORTS = ("moe_abi_version", "moe_route", "moe_permute", "moe_workspace_bytes",
            "moe_last_error", "moe_backward", "moe_backward_workspace_bytes",
            "moe_saved_bytes", "moe_forward_train", "moe_backward_saved",
            "moe_block_backward", "moe_block_forward_train", "moe_block_backward_saved",
-           "moe_set_gemm_path")
+           "moe_set_gemm_path", "moe_forward_noalloc")
 STAGES = {"router": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4,
           "bwd_recompute": 5, "bwd_dh": 6, "bwd_dx": 7, "bwd_wgrad": 8}
 
@@ -75,6 +75,9 @@ def load(path: str | None = None):
     lib.moe_set_stage_events.argtypes = [I32, V, V]
     lib.moe_set_gemm_path.restype = ctypes.c_int
     lib.moe_set_gemm_path.argtypes = [I32]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int,
+                                        V, V, V, V, V]
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [V, V, V, V, V, I64, I64, I64, I32, I32, ctypes.c_int, F,
                                       V, V, SZ, V, V, V, V]
@@ -243,6 +246,22 @@ def forward(x, Wg, W1, W3, W2, K: int):
     L = Layer(x.shape[0], d, d_ff, n, K, x.dtype, x.device)
     y = L.forward(x, Wg, W1, W3, W2)
     return y, L.idx, L.gate, L.counts
+
+
+def forward_noalloc(x, Wg, W1, W3, W2, K: int, y, idx=None, gate=None, counts=None):
+    """moe_forward_noalloc: the layer into the caller's y (and the optional
+    routing outputs) with the library's static scratch instead of a
+    workspace; allocates nothing."""
+    n, d_ff, d = W1.shape
+    L = Layer.__new__(Layer)
+    L.T, L.d, L.d_ff, L.n, L.K, L.dtype = x.shape[0], d, d_ff, n, K, x.dtype
+    px = L._args(x, Wg, W1, W3, W2)
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("y must match x in shape and dtype")
+    st = load().moe_forward_noalloc(*px, L.T, d, d_ff, n, K, _dtype_code(x), _dev(y, "y"),
+                                    _ptr(idx), _ptr(gate), _ptr(counts), _stream(x.device))
+    _check(st, "moe_forward_noalloc")
+    return y
 
 
 def block_forward(x, Wg, W1, W3, W2, K: int, eps: float):

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "moe.h"
@@ -258,14 +259,50 @@ size_t saved_bytes_for(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K)
     return L.U + align256((size_t)T * (size_t)d * 2);
 }
 
+// ---- the static scratch of moe_forward_noalloc -----------------------------
+// For callers that cannot allocate device memory: a file-scope device array
+// stands in for the workspace.  Each device that the library runs on holds
+// its own copy until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.  Every call on one device shares its array; no kernel of
+// the forward needs the workspace cleared, so nothing is zeroed.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d >= %d", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc: hipGetSymbolAddress");
+        if (!p) return fail(MOE_ERR_HIP, "moe_forward_noalloc: scratch has no device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
                            const void* w3, const void* w2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, float eps,
                            void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
                            float* gate_out, int32_t* counts_out, void* stream,
-                           void* saved = nullptr, size_t saved_bytes = 0) {
-    const char* fn = saved ? (block ? "moe_block_forward_train" : "moe_forward_train")
-                           : block ? "moe_block_forward" : "moe_forward";
+                           void* saved = nullptr, size_t saved_bytes = 0,
+                           bool static_scratch = false) {
+    const char* fn = static_scratch ? "moe_forward_noalloc"
+                     : saved ? (block ? "moe_block_forward_train" : "moe_forward_train")
+                             : block ? "moe_block_forward" : "moe_forward";
     moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
     if (st != MOE_OK) return st;
     if (saved) {
@@ -298,7 +335,13 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                     "< 2^30); split the tokens into several calls",
                     fn);
     const Layout L = layout(T, d, d_ff, n, K, dt);
-    if (T > 0) {
+    if (static_scratch && L.total > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: these sizes need %zu bytes of scratch, the library's static scratch "
+                    "holds %zu (enough for 256 tokens at d = 4096, d_ff = 14336, n = 8, K = 2); "
+                    "call moe_forward with a workspace instead",
+                    fn, L.total, kScratchBytes);
+    if (T > 0 && !static_scratch) {
         if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
         if (!aligned(workspace, 256))
             return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
@@ -324,6 +367,10 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                 return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved overlaps another argument", fn);
     }
     if (T == 0) return MOE_OK;
+    if (static_scratch) {
+        st = scratch_address(&workspace);
+        if (st != MOE_OK) return st;
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
@@ -715,6 +762,15 @@ moe_status_t moe_set_stage_events(int32_t stage, void* start_event, void* end_ev
     g_ev_start[stage] = static_cast<hipEvent_t>(start_event);
     g_ev_end[stage] = static_cast<hipEvent_t>(end_event);
     return MOE_OK;
+}
+
+moe_status_t moe_forward_noalloc(const void* x, const void* w_g, const void* w1,
+                                 const void* w3, const void* w2, int64_t T, int64_t d,
+                                 int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, void* y,
+                                 int32_t* idx_out, float* gate_out, int32_t* counts_out,
+                                 void* stream) {
+    return layer_forward(false, x, w_g, w1, w3, w2, T, d, d_ff, n, K, dt, 0.0f, y, nullptr, 0,
+                         idx_out, gate_out, counts_out, stream, nullptr, 0, true);
 }
 
 moe_status_t moe_set_gemm_path(int32_t path) {

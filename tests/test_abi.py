@@ -228,3 +228,22 @@ def test_gemm_path_hook(lib):
     for p in (B.MOE_GEMM_TILED, B.MOE_GEMM_STREAM, B.MOE_GEMM_AUTO):
         assert lib.moe_set_gemm_path(p) == B.MOE_OK
 
+
+def test_noalloc_validation(lib):
+    """moe_forward_noalloc checks its arguments, and that the sizes fit the
+    static scratch, before touching the device."""
+    def call(T=16, d=4096, d_ff=14336, x=FAKE, y=FAKE * 64, dt=B.MOE_BF16):
+        return lib.moe_forward_noalloc(x, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d, d_ff, 8,
+                                       2, dt, y, None, None, None, None)
+    big = lib.moe_workspace_bytes(4096, 4096, 14336, 8, 2, B.MOE_BF16)
+    assert big > 64 << 20
+    assert call(T=4096) == B.MOE_ERR_UNSUPPORTED
+    msg = lib.moe_last_error().decode()
+    assert "moe_forward_noalloc" in msg and "static scratch" in msg and str(big) in msg
+    assert lib.moe_workspace_bytes(256, 4096, 14336, 8, 2, B.MOE_BF16) <= 64 << 20
+    assert lib.moe_workspace_bytes(512, 4096, 14336, 8, 2, B.MOE_BF16) > 64 << 20
+    assert call(T=512) == B.MOE_ERR_UNSUPPORTED
+    assert call(x=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(y=FAKE + 8) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d=4095) == B.MOE_ERR_UNSUPPORTED
+    assert call(T=0, x=None, y=None) == B.MOE_OK
