@@ -143,6 +143,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     static_assert(STAGE_BYTES <= STG, "stage fits (STG: bytes of each stage object)");
     static_assert(!(GATEUP && (AKR || BKR)), "K-row operands only in plain products");
     static_assert(KD == BK || (KD == 32 && AKR && BKR), "32-deep steps: K-row operands only");
+    // the K-row swizzle XORs the chunk index with up to 12: rows of >= 16 chunks
+    static_assert((!AKR || BM >= 128) && (!BKR || BN >= 128), "K-row tiles of >= 128 columns");
 
     const int Kdim = t.Kdim, N = t.N, rows = t.rows, n0 = t.n0;
     const int tid = threadIdx.x;
