@@ -1,0 +1,115 @@
+"""Register spills of the MFMA kernels, from the gfx950 assembly of this
+repository's own sources (hipcc -S, no GPU needed).
+
+* No scratch (spill) instruction may sit inside a loop that issues MFMAs:
+  such a loop is the kernel's hot path.
+* Every kernel has a zero private segment (no spills at all), except the two
+  gate/up variants whose epilogue evaluates SiLU (H, and H plus [a | b]).
+  Their main loop holds 100 VGPRs plus 256 accumulator AGPRs; the register
+  allocator parks one lane offset shared by the loader and the epilogue in
+  scratch once per tile (a store before the K loop, reloads in the epilogue),
+  which this test bounds to a few dwords.
+"""
+import concurrent.futures
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_14_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["gemm_bf16.hip", "gemm_skinny.hip", "gemm_krow_stream.hip", "backward.hip"]
+# kernels allowed a small private segment: gate/up with the SiLU epilogue
+# (template EPI 0: H; EPI 3: H and [a | b]); bytes per lane at most
+ALLOWED = {r"gemm_bf16_kernelILb1ELb[01]ELi4ELi0ELb0": 16,
+           r"gemm_bf16_kernelILb1ELb[01]ELi4ELi3ELb0": 32}
+
+
+def _assemble(src, tmp):
+    out = os.path.join(tmp, src + ".s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I",
+           os.path.join(ROOT, "include"), "-I", CSRC, "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-Wno-unused-command-line-argument", "--cuda-device-only",
+           "-S", os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return src, open(out).read()
+
+
+def _kernels(asm):
+    """(name, body lines, private segment bytes) of every kernel."""
+    lines = asm.split("\n")
+    starts = [i for i, l in enumerate(lines)
+              if re.match(r"^_Z\S+:", l) and ".type" in lines[i - 1] + lines[i - 2] + lines[i - 3]]
+    out = []
+    for i in starts:
+        name = lines[i].split(":")[0]
+        j = i + 1
+        while j < len(lines) and not lines[j].strip().startswith(".Lfunc_end"):
+            j += 1
+        m = re.search(r"\.amdhsa_kernel " + re.escape(name) + r"\n(.*?)\.end_amdhsa_kernel",
+                      asm, re.S)
+        if not m:
+            continue
+        seg = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(1)).group(1))
+        out.append((name, lines[i:j], seg))
+    return out
+
+
+def _mfma_loops(body):
+    """The loops (by header block) whose own blocks issue MFMAs, as lists of
+    lines.  Loop membership comes from the compiler's block annotations
+    ("=>This ... Loop Header" on a header, "in Loop: Header=..." on the other
+    blocks of its innermost loop), so rotated loops count too."""
+    blocks, cur_hdr, cur = {}, None, []
+
+    def close():
+        if cur_hdr is not None:
+            blocks.setdefault(cur_hdr, []).extend(cur)
+
+    for l in body:
+        m_lab = re.match(r"^(\.LBB\d+_\d+):(.*)$", l) or re.match(r"^; %bb\.\d+:(.*)$", l)
+        if m_lab:
+            close()
+            cur = []
+            ann = m_lab.group(m_lab.lastindex)
+            h = re.search(r"Loop Header: Depth", ann)
+            inl = re.search(r"in Loop: Header=(BB\d+_\d+)", ann)
+            if h:
+                cur_hdr = m_lab.group(1).lstrip(".L")
+            elif inl:
+                cur_hdr = inl.group(1)
+            else:
+                cur_hdr = None
+        cur.append(l)
+    close()
+    return [lines for lines in blocks.values() if any("v_mfma" in x for x in lines)]
+
+
+@pytest.fixture(scope="module")
+def assembly(tmp_path_factory):
+    tmp = str(tmp_path_factory.mktemp("asm"))
+    with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
+        return dict(ex.map(lambda s: _assemble(s, tmp), SOURCES))
+
+
+def test_no_spill_inside_mfma_loops(assembly):
+    checked = 0
+    for src, asm in assembly.items():
+        for name, body, _ in _kernels(asm):
+            for lines in _mfma_loops(body):
+                checked += 1
+                bad = [x.strip() for x in lines if "scratch_" in x]
+                assert not bad, f"{src} {name}: spill inside an MFMA loop: {bad[:3]}"
+    assert checked >= 20
+
+
+def test_private_segments(assembly):
+    seen_gateup = 0
+    for src, asm in assembly.items():
+        for name, _, seg in _kernels(asm):
+            limit = next((v for k, v in ALLOWED.items() if re.search(k, name)), 0)
+            seen_gateup += limit > 0
+            assert seg <= limit, f"{src} {name}: {seg} bytes of scratch per lane"
+    assert seen_gateup == 4
