@@ -17,16 +17,16 @@
 //             (fp32; only the tiles of the last round -- rows from R0 on --
 //             are split along K, and the combine adds their partial sums).
 //
-// Tile shapes.  Gate/up: four waves, each holding a 128 x 128 fp32
+// Tile shapes.  Gate/up and down: four waves, each holding a 128 x 128 fp32
 // accumulator (4 x 4 MFMA tiles of 32 x 32, 256 accumulators per lane, in
 // AGPRs, one wave per SIMD); per 16-deep K sub-step a wave reads 4 A and 4 B
-// fragments from LDS for 16 MFMAs.  Down: eight waves of 128 x 64 (two per
-// SIMD, so a wave stalled on a load does not idle its SIMD's MFMA unit).  A
-// workgroup owns 256 token rows x 256 B rows (waves 2 x 2 or 2 x 4), or --
-// for an expert's last row tile when it has at most 128 rows -- 128 token
-// rows x 512 B rows (waves 1 x 4 or 1 x 8), the same MFMA work over twice
-// the columns, so a short tail costs half a tile instead of a whole one.  Both
-// operands are K-contiguous ([out][in] weights), the per-lane 8-element K
+// fragments from LDS for 16 MFMAs.  The backward's K-row products run eight
+// waves of 128 x 64 (two per SIMD).  A workgroup owns 256 token rows x 256 B
+// rows (waves 2 x 2 or 2 x 4), or -- for an expert's last row tile when it
+// has at most 128 rows -- 128 token rows x 512 B rows (waves 1 x 4 or
+// 1 x 8), the same MFMA work over twice the columns, so a short tail costs
+// half a tile instead of a whole one.  Both operands are K-contiguous
+// ([out][in] weights), the per-lane 8-element K
 // run each MFMA operand wants; the weights are the MFMA's first operand, so
 // a lane ends up owning 4 contiguous output columns.
 //
@@ -34,11 +34,12 @@
 // 16-byte chunk XOR-swizzled by (row / 2) % 8 so that the fragment reads of
 // 16 consecutive rows hit distinct banks).  A stage is filled by buffer loads
 // with the LDS flag (global -> LDS, no registers, no LDS write instructions),
-// issued one step ahead during the first MFMAs of a step; one barrier per
-// step waits for them (gate/up also prefetches its weight rows into L2 two
-// steps ahead).  Rows past the tile are clamped to a valid row (never
-// stored); a K tail and the step past the end load through an out-of-range
-// offset, which writes zeros.  Outputs leave through LDS as whole 16-byte
+// issued one step ahead among the MFMAs of the first two sub-steps of a step;
+// one barrier per step waits for them (four-wave square tiles also prefetch
+// their weight rows into L2 two steps ahead).  Rows past the tile are clamped
+// to a valid row (never stored); a K tail and the step past the end load
+// through an out-of-range offset, which writes zeros.  Outputs leave through
+// LDS as whole 16-byte
 // chunks of rows, with non-temporal stores.
 //
 // The same tile body also runs the backward's products with K-row operands
@@ -240,7 +241,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // zero-size resource: every load is out of range and writes zeros, so the
     // issue pattern and the load count stay the same.  K tails: chunks past
     // Kdim get an out-of-range offset.
-    auto issue = [&](uint8_t* st, int kt) {
+    // Loads lo .. hi - 1 of the step's NLD (A loads first, then B loads).
+    auto issue = [&](uint8_t* st, int kt, int lo = 0, int hi = 1 << 30) {
         const bool live = kt < k_end;
         const int k0 = live ? kt * BK : 0;
         const uint32_t kb = (uint32_t)k0 * 2u;
@@ -250,6 +252,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         const int krow = t.krow0 + (live ? kt : 0) * KD;  // K row of tile row 0
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
+            if (i < lo || i >= hi) continue;
             if constexpr (AKR) {
                 const int r = krow + a_kr[i];
                 const uint32_t off =
@@ -267,6 +270,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         }
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
+            if (A_LD + i < lo || A_LD + i >= hi) continue;
             if constexpr (BKR) {
                 // the instruction's first row decides B1 or B3 (b_split is a
                 // multiple of the rows per instruction)
@@ -292,21 +296,22 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         }
     };
 
-    // Gate/up weight rows are prefetched into L2 two K steps ahead.  Each
-    // weight panel's K slice comes from HBM the first time a tile reaches it,
-    // and one step of LDS prefetch leaves that latency exposed (waiting on
-    // the B loads took ~19% of a wave's loop at T = 4096).  One 4-byte load
-    // per B row (one 128-byte line of the row's K slice) goes out after all
-    // stage loads of the step, into a register consumed a step later; loads
-    // complete in issue order, so the barrier's vmcnt(1) leaves exactly that
-    // load outstanding.  Measured: gate/up 2-4% faster; the down projection
-    // was slower with it.
-    constexpr bool TOUCH = GATEUP && SH::BM == 256 && SH::BN == 256 && NW == 4;
+    // Weight rows of four-wave square tiles are prefetched into L2 two K
+    // steps ahead.  Each weight panel's K slice comes from HBM the first time
+    // a tile reaches it, and one step of LDS prefetch leaves that latency
+    // exposed (waiting on the B loads took ~19% of a wave's loop at
+    // T = 4096).  One 4-byte load per B row (one 128-byte line of the row's K
+    // slice) goes out after all stage loads of the step, into a register
+    // consumed a step later; loads complete in issue order, so the barrier's
+    // vmcnt(1) leaves exactly that load outstanding.  Measured: gate/up 2-4%
+    // faster, the four-wave down projection 4-5% (on the eight-wave one it
+    // was slower).
+    constexpr bool TOUCH = SH::BM == 256 && SH::BN == 256 && NW == 4 && !AKR && !BKR;
     auto touch = [&](int kt2) -> uint32_t {
         if constexpr (TOUCH) {
-            const int r = wid * 64 + lane;  // B tile row: W1 rows, then W3 rows
-            const bool w3 = wid >= 2;       // wave-uniform
-            const int col = n0 + (r & (BN / 2 - 1));
+            const int r = wid * 64 + lane;  // B tile row (gate/up: W1 rows, then W3 rows)
+            const bool w3 = GATEUP && wid >= 2;  // wave-uniform
+            const int col = n0 + (GATEUP ? (r & (BN / 2 - 1)) : r);
             const uint32_t off =
                 KTAIL && kt2 * BK >= Kdim
                     ? 0x80000000u
@@ -431,17 +436,26 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // loads of step kt + 1 go into stage Y, free since the last barrier);
     // then the barrier publishes Y, whose first fragments are read while the
     // last MFMAs of X run.
+    // Four-wave tiles spread the step's loads over sub-steps 1 and 2: bunched
+    // into one sub-step (one load per MFMA) they fill the texture units'
+    // address and command FIFOs and stall the SIMD's only wave between its
+    // MFMAs (FIFO-full stall counters 10x those of hipBLASLt's kernel on the
+    // same product).  Measured: gate/up 3.3-6.7% faster; the eight-wave
+    // tiles, whose SIMDs hold a second wave, were not.
+    constexpr int SPREAD = NW == 4 && KS > 2 ? 2 : 1;
     bf16x8_t fa[2][TM], fb[2][TN];
     auto step = [&](const uint8_t* X, uint8_t* Y, int kt) {
-        issue(Y, kt + 1);
         uint32_t touch_now = 0;
 #pragma unroll
         for (int sub = 1; sub < KS; ++sub) {
+            const int lo = sub <= SPREAD ? (sub - 1) * NLD / SPREAD : NLD;
+            const int hi = sub <= SPREAD ? sub * NLD / SPREAD : NLD;
+            if (hi > lo) issue(Y, kt + 1, lo, hi);
             read_frags(X, sub, fa[sub & 1], fb[sub & 1]);
             mfmas(fa[(sub - 1) & 1], fb[(sub - 1) & 1]);
-            interleave(sub == 1 ? NLD : 0);
+            interleave(hi - lo);
             __builtin_amdgcn_sched_barrier(0);
-            if (TOUCH && sub == 1) {  // after every stage load of the step
+            if (TOUCH && sub == SPREAD) {  // after every stage load of the step
                 touch_now = touch(kt + 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -867,8 +881,9 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
                                   int cus, int* split_meta, hipStream_t s) {
     if (!tiled_fits(A_src_rows, Kdim, N) || (!gateup && (cus < 1 || !split_meta)))
         return hipErrorInvalidValue;
-    // Gate/up: four waves of 128 x 128.  Down: eight waves of 128 x 64 (two
-    // per SIMD), measured 2% faster there and 3.5% slower on gate/up.
+    // Four waves of 128 x 128 for both (measured against eight waves of
+    // 128 x 64 for the down projection: 4-5% faster once the loads are
+    // spread and its weight rows prefetched into L2).
     const int GM = 8;
     if (gateup)
         return launch_tiled<true, 4>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
@@ -876,7 +891,7 @@ hipError_t launch_gemm_bf16_tiled(bool gateup, const uint16_t* A, int64_t A_src_
     // Down tails of at most 128 rows run wide as on gate/up (measured: 1%
     // faster on the 32-layer stack at T = 2048, unchanged at T = 4096).  Up
     // to `splits` K splits for the last round's tiles only (see the kernel).
-    return launch_tiled<false, 8>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
+    return launch_tiled<false, 4>(A, A_src_rows, perm, K, B1, B3, offsets, n, A_rows, Kdim, N,
                                   C, GM, splits, s, nullptr, 128, cus, split_meta);
 }
 
