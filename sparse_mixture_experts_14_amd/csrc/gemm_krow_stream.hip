@@ -36,7 +36,6 @@ constexpr int PMAX = 16;  // expert rows per pass
 constexpr int KC = 16;    // K rows per chunk
 constexpr uint32_t OOB_K = 0x80000000u;  // buffer offset past every range: loads 0
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_k(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,

@@ -4,12 +4,15 @@
 // G(x) = Softmax(TopK(x . W_g)); TopK leaves the K largest logits and sets the
 // rest to -inf, so the softmax normalises over the K kept logits only.
 //
-// One workgroup of 256 threads per token.  Thread i reads the 16-byte chunks
-// i, i+256, ... of the token's row, multiplies each element with the matching
-// row of W_g (n contiguous values), and keeps n fp32 partial sums; a butterfly
-// inside each wave and a fixed-order sum of the 4 waves' partials in LDS give
-// the n logits (fp32, never rounded to bf16, same order every call).  Thread
-// 0 then takes the TopK (ties to the lower index) and the softmax.
+// Logits are fp32 sums of exact bf16 (or fp32) products, never rounded to
+// bf16, summed in one fixed order (deterministic).  TopK and the softmax run
+// across the lanes of one wavefront: a token's logits sit in a group of lanes
+// (lane e holds expert e), and each of the K rounds is an argmax butterfly
+// over the group on (logit, index) pairs -- the larger logit wins, equal
+// logits go to the lower index -- after which the winner's lane drops out.
+// The lanes of the group then hold the K selected (index, logit) pairs in
+// rank order; lane j < K writes slot j with the softmax weight
+// exp(l_j - l_0) / sum_i exp(l_i - l_0).
 //
 // The pre-normalised variant (a layer of a residual stack) also accumulates
 // sum(x^2), scales the logits by rstd = 1/sqrt(mean(x^2) + eps) -- the same
@@ -78,6 +81,57 @@ __device__ __forceinline__ void axpy_row(const TIn* __restrict__ w, int n, float
     }
 }
 
+// TopK and softmax of one token whose n <= G logits sit in a group of G
+// lanes (G a power of two <= 64; lane e of the group holds expert e's logit,
+// lanes e >= n hold nothing).  Every lane of the group ends with the same
+// sel / val; lane j < K of the group writes slot j of the token's idx and
+// gate rows.
+template <int G>
+__device__ __forceinline__ void wave_topk_softmax(float l, int e, int n, int K,
+                                                  int32_t* __restrict__ idx_row,
+                                                  float* __restrict__ gate_row) {
+    bool live = e < n;  // still selectable
+    int sel[8];
+    float val[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+            float v = live ? l : -INFINITY;
+            int i = live ? e : 0x7fff;
+#pragma unroll
+            for (int m = 1; m < G; m <<= 1) {
+                const float ov = __shfl_xor(v, m, kWave);
+                const int oi = __shfl_xor(i, m, kWave);
+                if (ov > v || (ov == v && oi < i)) {
+                    v = ov;
+                    i = oi;
+                }
+            }
+            sel[j] = i;
+            val[j] = v;
+            if (i == e) live = false;
+        }
+    }
+    // softmax over the kept logits; val[0] is the largest
+    float g[8];
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+            g[j] = expf(val[j] - val[0]);
+            z += g[j];
+        }
+    }
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < K && e == j) {
+            idx_row[j] = sel[j];
+            gate_row[j] = g[j] * rz;
+        }
+    }
+}
+
 template <typename TIn, int NE, bool NORM>
 __global__ __launch_bounds__(256) void router_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, int64_t T, int d, int n,
@@ -117,61 +171,20 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
     __syncthreads();
 
-    if (threadIdx.x == 0) {
-        float l[NE];
-#pragma unroll
-        for (int e = 0; e < NE; ++e)
-            l[e] = (part[0][e] + part[1][e]) + (part[2][e] + part[3][e]);
+    // Wave 0: lane e < n forms logit e (fixed-order sum of the 4 waves'
+    // partials) and the wave takes TopK and the softmax.
+    if (wv == 0) {
         float rstd = 1.0f;
         if (NORM) {
             const float sst = (part[0][NE] + part[1][NE]) + (part[2][NE] + part[3][NE]);
             rstd = 1.0f / sqrtf(sst / (float)d + eps);
-#pragma unroll
-            for (int e = 0; e < NE; ++e) l[e] *= rstd;
-            s_rstd = rstd;
+            if (lane == 0) s_rstd = rstd;
         }
-        // TopK: K rounds of "largest logit not yet taken"; a later expert
-        // needs a strictly larger logit, so ties go to the lower index.
-        uint64_t taken = 0;
-        int sel[8];
-        float val[8];
+        float l = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < K) {
-                int best = -1;
-                float bv = 0.0f;
-#pragma unroll
-                for (int e = 0; e < NE; ++e) {
-                    if (e < n && !((taken >> e) & 1ull)) {
-                        if (best < 0 || l[e] > bv) {
-                            best = e;
-                            bv = l[e];
-                        }
-                    }
-                }
-                taken |= 1ull << best;
-                sel[j] = best;
-                val[j] = bv;
-            }
-        }
-        // Softmax over the kept logits; val[0] is the largest.
-        float g[8];
-        float z = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < K) {
-                g[j] = expf(val[j] - val[0]);
-                z += g[j];
-            }
-        }
-        const float rz = 1.0f / z;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < K) {
-                idx[t * K + j] = sel[j];
-                gate[t * K + j] = g[j] * rz;
-            }
-        }
+        for (int e = 0; e < NE; ++e)
+            if (e == lane) l = ((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) * rstd;
+        wave_topk_softmax<NE>(l, lane, n, K, idx + t * K, gate + t * K);
     }
 
     if (NORM) {
@@ -188,171 +201,210 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
 }
 
+// Halving exchanges over lane bits 5, 4, ..: V = 2^M values per lane in,
+// and lane l ends with the wave's full sum of value number l >> (6 - M)
+// (the xor-32 exchange halves the values a lane keeps, then xor-16, ...; the
+// remaining xor-(32 >> M) .. xor-1 butterfly completes the sums).  A fixed
+// order of adds: the result is deterministic.
+template <int M>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[1 << M], int lane) {
+#pragma unroll
+    for (int st = 0; st < M; ++st) {
+        const int mask = 32 >> st;
+        const int half = (1 << M) >> (st + 1);
+        const bool hi = lane & mask;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            // select values, not array slots (a select of slots becomes a
+            // dynamic index into the array)
+            const float lo_v = v[i], hi_v = v[half + i];
+            const float mine = hi ? hi_v : lo_v;
+            const float other = hi ? lo_v : hi_v;
+            v[i] = mine + __shfl_xor(other, mask, kWave);
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int mask = 32 >> M; mask >= 1; mask >>= 1) r += __shfl_xor(r, mask, kWave);
+    return r;
+}
+
 // Resident-weight variant (bf16, n = 8, d = 256 * ELEMS): thread i keeps
 // rows [i ELEMS, (i + 1) ELEMS) of W_g (8 bf16 = 16 bytes per row) in
-// registers and walks the tokens blockIdx.x, blockIdx.x + gridDim.x, ...,
-// prefetching the next token's slice of x while it reduces the current one.
-// W_g is then read once per workgroup instead of once per token.  Per token:
-// ELEMS * 8 fp32 FMAs per thread, a wave butterfly and a fixed-order sum of
-// the 4 waves' partials in LDS (deterministic), then thread 0 takes TopK
-// (ties to the lower index) and the softmax.  The pre-normalised variant
-// also sums x^2; every thread forms rstd from the same LDS partials (same
-// order, same value) and writes its slice of u.
-template <int ELEMS, bool NORM>
+// registers, so W_g is read once per workgroup, and the workgroup walks
+// batches of TB tokens (batch b, b + gridDim.x, ...), prefetching the next
+// batch's slices of x while it reduces the current one.  Per batch: ELEMS *
+// 4 * TB bf16-pair dot products (fp32 sums) per thread; one wave
+// reduce-scatter of the TB * 8
+// partial logits; a fixed-order sum of the 4 waves' partials in LDS
+// (deterministic); then wave w takes TopK and the softmax of token w of the
+// batch in its lanes 0..7.  The pre-normalised variant also reduces the TB
+// sums of x^2; every thread forms each token's rstd from the same LDS
+// partials (same order, same value) and writes its slices of u.
+template <int ELEMS, int TB, bool NORM>
 __global__ __launch_bounds__(256) void router_resident_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int64_t T, int d, int K,
     float eps, int32_t* __restrict__ idx, float* __restrict__ gate,
     uint16_t* __restrict__ u_out) {
     constexpr int NE = 8;
-    constexpr int XV = ELEMS / 8;  // 16-byte chunks of x per thread
-    __shared__ float part[2][4][NE + 1];
+    constexpr int XV = ELEMS / 8;  // 16-byte chunks of x per thread and token
+    constexpr int M = TB == 4 ? 5 : TB == 2 ? 4 : 3;  // log2(TB * NE)
+    constexpr int MS = TB == 4 ? 2 : TB == 2 ? 1 : 0;  // log2(TB)
+    static_assert(TB == 1 || TB == 2 || TB == 4, "batches of 1, 2 or 4 tokens");
+    __shared__ float part[2][4][TB * NE];
+    __shared__ float part_ss[2][4][TB];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     const int k0 = tid * ELEMS;
-    uint4 w[ELEMS];
+    // W_g rows k0 + 2p and k0 + 2p + 1 packed per expert as bf16 pairs, the
+    // operand layout of v_dot2_f32_bf16 (x holds its pairs natively): one
+    // dot2 adds both products, and W_g stays packed in 4 ELEMS registers.
+    uint32_t wp[ELEMS / 2][NE];
 #pragma unroll
-    for (int j = 0; j < ELEMS; ++j) w[j] = *reinterpret_cast<const uint4*>(wg + (int64_t)(k0 + j) * NE);
-    auto wget = [&](int j, int e) {
-        const uint32_t v = e < 2 ? w[j].x : e < 4 ? w[j].y : e < 6 ? w[j].z : w[j].w;
-        return (e & 1) ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
-    };
-    auto load = [&](uint4(&xv)[XV], int64_t t) {
-        const uint4* p = reinterpret_cast<const uint4*>(x + t * (int64_t)d + k0);
+    for (int p = 0; p < ELEMS / 2; ++p) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(wg + (int64_t)(k0 + 2 * p) * NE);
+        const uint4 hi = *reinterpret_cast<const uint4*>(wg + (int64_t)(k0 + 2 * p + 1) * NE);
+        const uint32_t l4[4] = {lo.x, lo.y, lo.z, lo.w}, h4[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-        for (int c = 0; c < XV; ++c) xv[c] = p[c];
-    };
-    auto xget = [&](const uint4(&xv)[XV], int j) {
-        const uint4& c = xv[j / 8];
-        const int e = j % 8;
-        const uint32_t v = e < 2 ? c.x : e < 4 ? c.y : e < 6 ? c.z : c.w;
-        return (e & 1) ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
-    };
-    int64_t t = blockIdx.x;
-    uint4 xv[XV];
-    if (t < T) load(xv, t);
-    for (int par = 0; t < T; t += gridDim.x, par ^= 1) {
-        uint4 xn[XV];
-        const int64_t tn = t + gridDim.x;
-        if (tn < T) load(xn, tn);
-        float acc[NE];
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
-        float ss = 0.0f;
-#pragma unroll
-        for (int j = 0; j < ELEMS; ++j) {
-            const float xf = xget(xv, j);
-            if (NORM) ss = fmaf(xf, xf, ss);
-#pragma unroll
-            for (int e = 0; e < NE; ++e) acc[e] = fmaf(xf, wget(j, e), acc[e]);
+        for (int q = 0; q < 4; ++q) {
+            wp[p][2 * q] = __builtin_amdgcn_perm(h4[q], l4[q], 0x05040100u);
+            wp[p][2 * q + 1] = __builtin_amdgcn_perm(h4[q], l4[q], 0x07060302u);
         }
-        // Reduce-scatter over the wave: the xor-32/16/8 exchanges halve the
-        // values a lane keeps (4 + 2 + 1 shuffles), the xor-4/2/1 butterfly
-        // finishes the sums; lane 8 e' then holds logit e' = lane bits 5..3.
-        float v4[4], v2[2];
-        const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mine = b5 ? acc[4 + i] : acc[i], other = b5 ? acc[i] : acc[4 + i];
-            v4[i] = mine + __shfl_xor(other, 32, kWave);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float mine = b4 ? v4[2 + i] : v4[i], other = b4 ? v4[i] : v4[2 + i];
-            v2[i] = mine + __shfl_xor(other, 16, kWave);
-        }
-        float v1 = (b3 ? v2[1] : v2[0]) + __shfl_xor(b3 ? v2[0] : v2[1], 8, kWave);
-        v1 += __shfl_xor(v1, 4, kWave);
-        v1 += __shfl_xor(v1, 2, kWave);
-        v1 += __shfl_xor(v1, 1, kWave);
-        if (NORM) ss = wave_sum(ss);
-        if ((lane & 7) == 0) part[par][wv][lane >> 3] = v1;
-        if (NORM && lane == 0) part[par][wv][NE] = ss;
-        __syncthreads();
-        float rstd = 1.0f;
-        if (NORM) {
-            const float sst = (part[par][0][NE] + part[par][1][NE]) +
-                              (part[par][2][NE] + part[par][3][NE]);
-            rstd = 1.0f / sqrtf(sst / (float)d + eps);
-        }
-        if (tid == 0) {
-            float l[NE];
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-                l[e] = ((part[par][0][e] + part[par][1][e]) + (part[par][2][e] + part[par][3][e])) *
-                       rstd;
-            uint32_t taken = 0;
-            int sel[8];
-            float val[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < K) {
-                    int best = -1;
-                    float bv = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < NE; ++e) {
-                        if (!((taken >> e) & 1u) && (best < 0 || l[e] > bv)) {
-                            best = e;
-                            bv = l[e];
-                        }
-                    }
-                    taken |= 1u << best;
-                    sel[j] = best;
-                    val[j] = bv;
-                }
-            }
-            float g[8];
-            float z = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < K) {
-                    g[j] = expf(val[j] - val[0]);
-                    z += g[j];
-                }
-            }
-            const float rz = 1.0f / z;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < K) {
-                    idx[t * K + j] = sel[j];
-                    gate[t * K + j] = g[j] * rz;
-                }
-            }
-        }
-        if (NORM) {
-            uint4* up = reinterpret_cast<uint4*>(u_out + t * (int64_t)d + k0);
-#pragma unroll
-            for (int c = 0; c < XV; ++c) {
-                uint4 o;
-                o.x = pack_bf16x2(xget(xv, 8 * c + 0) * rstd, xget(xv, 8 * c + 1) * rstd);
-                o.y = pack_bf16x2(xget(xv, 8 * c + 2) * rstd, xget(xv, 8 * c + 3) * rstd);
-                o.z = pack_bf16x2(xget(xv, 8 * c + 4) * rstd, xget(xv, 8 * c + 5) * rstd);
-                o.w = pack_bf16x2(xget(xv, 8 * c + 6) * rstd, xget(xv, 8 * c + 7) * rstd);
-                up[c] = o;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < XV; ++c) xv[c] = xn[c];
     }
+    // tokens past T read as zeros (their outputs are not written)
+    auto load = [&](uint4(&xv)[TB][XV], int64_t t0) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+            const uint4* p = reinterpret_cast<const uint4*>(x + (t0 + b) * (int64_t)d + k0);
+#pragma unroll
+            for (int c = 0; c < XV; ++c) xv[b][c] = t0 + b < T ? p[c] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto xpair = [&](const uint4(&xv)[XV], int p) {  // elements 2p, 2p + 1 of the slice
+        const uint4& c = xv[p / 4];
+        const int q = p % 4;
+        return __builtin_bit_cast(bf16x2_t, q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w);
+    };
+    const int64_t nb = (T + TB - 1) / TB;
+    int64_t bt = blockIdx.x;
+    uint4 xv[TB][XV];
+    if (bt < nb) load(xv, bt * TB);
+    for (int par = 0; bt < nb; bt += gridDim.x, par ^= 1) {
+        const int64_t t0 = bt * TB;
+        uint4 xn[TB][XV];
+        if (bt + gridDim.x < nb) load(xn, (bt + gridDim.x) * TB);
+        float acc[TB * NE];
+        float ss[TB];
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+            ss[b] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[b * NE + e] = 0.0f;
+#pragma unroll
+            for (int p = 0; p < ELEMS / 2; ++p) {
+                const bf16x2_t xp2 = xpair(xv[b], p);
+                if (NORM) ss[b] = __builtin_amdgcn_fdot2_f32_bf16(xp2, xp2, ss[b], false);
+#pragma unroll
+                for (int e = 0; e < NE; ++e)
+                    acc[b * NE + e] = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2_t, wp[p][e]), xp2, acc[b * NE + e], false);
+            }
+        }
+        // lane l: the wave's sum of logit (l >> (6 - M)) = token l >> (9 - M),
+        // expert (l >> (6 - M)) % 8
+        const float lw = wave_reduce_scatter<M>(acc, lane);
+        if ((lane & ((1 << (6 - M)) - 1)) == 0) part[par][wv][lane >> (6 - M)] = lw;
+        if (NORM) {
+            const float sw = wave_reduce_scatter<MS>(ss, lane);
+            if ((lane & ((1 << (6 - MS)) - 1)) == 0) part_ss[par][wv][lane >> (6 - MS)] = sw;
+        }
+        __syncthreads();
+        float rstd[TB];
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+            rstd[b] = 1.0f;
+            if (NORM) {
+                const float sst = (part_ss[par][0][b] + part_ss[par][1][b]) +
+                                  (part_ss[par][2][b] + part_ss[par][3][b]);
+                rstd[b] = 1.0f / sqrtf(sst / (float)d + eps);
+            }
+        }
+        if (wv < TB && t0 + wv < T) {  // wave w: token t0 + w, lane e < 8: expert e
+            const int e = lane & 7;
+            float rs = rstd[0];
+#pragma unroll
+            for (int b = 1; b < TB; ++b)
+                if (b == wv) rs = rstd[b];
+            const int vi = wv * NE + e;
+            const float l = ((part[par][0][vi] + part[par][1][vi]) +
+                             (part[par][2][vi] + part[par][3][vi])) * rs;
+            wave_topk_softmax<8>(l, lane < 8 ? e : NE, NE, K, idx + (t0 + wv) * K,
+                                 gate + (t0 + wv) * K);
+        }
+        if (NORM) {
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                if (t0 + b >= T) continue;
+                uint4* up = reinterpret_cast<uint4*>(u_out + (t0 + b) * (int64_t)d + k0);
+                const float r = rstd[b];
+#pragma unroll
+                for (int c = 0; c < XV; ++c) {
+                    float f[8];
+                    unpack_bf16x8(xv[b][c], f);
+                    uint4 o;
+                    o.x = pack_bf16x2(f[0] * r, f[1] * r);
+                    o.y = pack_bf16x2(f[2] * r, f[3] * r);
+                    o.z = pack_bf16x2(f[4] * r, f[5] * r);
+                    o.w = pack_bf16x2(f[6] * r, f[7] * r);
+                    up[c] = o;
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int c = 0; c < XV; ++c) xv[b][c] = xn[b][c];
+    }
+}
+
+// Batches of 4 tokens (2 at d = 8192, where W_g alone holds 64 registers
+// per thread), at most 512 workgroups; up to 256 tokens, one token per
+// workgroup (measured: 4-token batches route T = 4096 in 18.8 us instead of
+// 24.9, T = 16384 in 41 instead of 74; at T = 16, 1-token batches take
+// 7.1 us, 4-token ones 8.4).
+template <int ELEMS, bool NORM>
+void launch_router_resident_d(int tb, dim3 grid, hipStream_t s, const uint16_t* xp,
+                              const uint16_t* wp, int64_t T, int d, int K, float eps,
+                              int32_t* idx, float* gate, uint16_t* up) {
+    const dim3 block(256);
+    if (tb == 1)
+        hipLaunchKernelGGL((router_resident_kernel<ELEMS, 1, NORM>), grid, block, 0, s, xp, wp,
+                           T, d, K, eps, idx, gate, up);
+    else if (tb == 2)
+        hipLaunchKernelGGL((router_resident_kernel<ELEMS, 2, NORM>), grid, block, 0, s, xp, wp,
+                           T, d, K, eps, idx, gate, up);
+    else if constexpr (ELEMS <= 16)
+        hipLaunchKernelGGL((router_resident_kernel<ELEMS, 4, NORM>), grid, block, 0, s, xp, wp,
+                           T, d, K, eps, idx, gate, up);
 }
 
 template <bool NORM>
 hipError_t launch_router_resident(const void* x, const void* wg, int64_t T, int d, int K,
                                   float eps, int32_t* idx, float* gate, void* u_out,
                                   hipStream_t s) {
-    const dim3 grid((unsigned)(T < 512 ? T : 512));
-    const dim3 block(256);
+    const int tb = T <= 256 ? 1 : d == 8192 ? 2 : 4;
+    const int64_t nb = (T + tb - 1) / tb;
+    const dim3 grid((unsigned)(nb < 512 ? nb : 512));
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* wp = static_cast<const uint16_t*>(wg);
     uint16_t* up = static_cast<uint16_t*>(u_out);
     if (d == 2048)
-        hipLaunchKernelGGL((router_resident_kernel<8, NORM>), grid, block, 0, s, xp, wp, T, d, K,
-                           eps, idx, gate, up);
+        launch_router_resident_d<8, NORM>(tb, grid, s, xp, wp, T, d, K, eps, idx, gate, up);
     else if (d == 4096)
-        hipLaunchKernelGGL((router_resident_kernel<16, NORM>), grid, block, 0, s, xp, wp, T, d,
-                           K, eps, idx, gate, up);
+        launch_router_resident_d<16, NORM>(tb, grid, s, xp, wp, T, d, K, eps, idx, gate, up);
     else
-        hipLaunchKernelGGL((router_resident_kernel<32, NORM>), grid, block, 0, s, xp, wp, T, d,
-                           K, eps, idx, gate, up);
+        launch_router_resident_d<32, NORM>(tb == 4 ? 2 : tb, grid, s, xp, wp, T, d, K, eps, idx,
+                                           gate, up);
     return hipGetLastError();
 }
 
