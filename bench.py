@@ -409,6 +409,90 @@ def bench_backward(args, w, dev, train=False):
     print(json.dumps(out), flush=True)
 
 
+# GEMM shapes of the layer (x[M][K] . W[N][K]^T): one expert's gate/up ([W1 ; W3], N =
+# 2 d_ff) and down products at the stack layer, at prefill and under skew (expert 0), and
+# the dense 8192-row products with the same flops as prefill.
+BLAS_SHAPES = [("gate_up_stack_expert", 512, 4096, 28672),
+               ("gate_up_prefill_expert", 1024, 4096, 28672),
+               ("gate_up_skew_expert0", 15872, 4096, 28672),
+               ("gate_up_dense_8192", 8192, 4096, 28672),
+               ("down_stack_expert", 512, 14336, 4096),
+               ("down_prefill_expert", 1024, 14336, 4096),
+               ("down_skew_expert0", 15872, 14336, 4096),
+               ("down_dense_8192", 8192, 14336, 4096)]
+
+
+def blas_calibration(reps: int = 20):
+    """hipBLASLt (torch.nn.functional.linear, bf16) on the layer's GEMM shapes with
+    N(0,1) tokens and N(0,1/K) weights: a calibration of what the library GEMM
+    reaches on this chip, not a part of the layer.  One JSON line per shape."""
+    import torch
+    import torch.nn.functional as F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, M, K, N in BLAS_SHAPES:
+        x = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(N, K, generator=g, device="cuda") / K ** 0.5).to(torch.bfloat16)
+        for _ in range(3):
+            F.linear(x, w)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            F.linear(x, w)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        ms = ts[len(ts) // 2]
+        print(json.dumps({"blas_shape": name, "M": M, "K": K, "N": N, "ms": round(ms, 4),
+                          "tflops": round(2.0 * M * K * N / ms / 1e9, 1)}), flush=True)
+        del x, w
+
+
+def dense_probe(T: int, reps: int = 10):
+    """The layer's own kernels on a dense problem: T positive tokens routed to
+    expert 0 (K = 1), so gate/up is one [T][4096] x [28672][4096]^T product and
+    down one [T][14336] x [4096][14336]^T -- the same work as the dense
+    library GEMMs of blas_calibration.  Stage times from the library's own
+    events.  One JSON line."""
+    import statistics
+
+    import torch
+
+    import sparse_mixture_experts_14_amd as moe
+    d, dff, n = 4096, 14336, 8
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(T, d, generator=g, device="cuda").abs().to(torch.bfloat16)
+    wg = torch.zeros(d, n, device="cuda")
+    wg[:, 0] = 1.0  # logit 0 = sum of |x| > 0 = every other logit
+    wg = wg.to(torch.bfloat16)
+    w1 = (torch.randn(n, dff, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    w3 = (torch.randn(n, dff, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(n, d, dff, generator=g, device="cuda") / dff ** 0.5).to(torch.bfloat16)
+    lay = moe.Layer(T, d, dff, n, 1, torch.bfloat16, "cuda")
+    ev = {st: (HipEvent(), HipEvent()) for st in ("gate_up", "down")}
+    res = {st: [] for st in ev}
+    for it in range(reps + 2):
+        for st, (a, b) in ev.items():
+            moe._lib.set_stage_events_raw(st, a.handle.value, b.handle.value)
+        lay.forward(x, wg, w1, w3, w2)
+        torch.cuda.synchronize()
+        if it >= 2:
+            for st, (a, b) in ev.items():
+                res[st].append(a.elapsed_ms(b))
+    for st in ev:
+        moe._lib.set_stage_events_raw(st)
+    if int(lay.counts[0]) != T:
+        raise SystemExit("dense probe: tokens did not all route to expert 0")
+    gu, dn = statistics.median(res["gate_up"]), statistics.median(res["down"])
+    print(json.dumps({"dense_probe_T": T, "gate_up_ms": round(gu, 4),
+                      "gate_up_tflops": round(4.0 * T * d * dff / gu / 1e9, 1),
+                      "down_ms": round(dn, 4),
+                      "down_tflops": round(2.0 * T * d * dff / dn / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +515,11 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward (all gradients of sum(dy * y)) instead of the "
                          "forward layer")
+    ap.add_argument("--blas-calibration", action="store_true",
+                    help="time hipBLASLt (torch F.linear) on the layer's GEMM shapes and exit")
+    ap.add_argument("--dense-probe", type=int, metavar="T", default=0,
+                    help="time the layer's gate/up and down kernels with T tokens all on "
+                         "expert 0 (the dense problem of --blas-calibration) and exit")
     ap.add_argument("--train", action="store_true",
                     help="time a training step: moe_forward_train, then moe_backward_saved "
                          "on its saved state")
@@ -457,6 +546,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.load()
+    if args.blas_calibration:
+        blas_calibration()
+        return
+    if args.dense_probe:
+        dense_probe(args.dense_probe)
+        return
     if args.backward or args.train:
         bench_backward(args, w, dev, train=args.train)
         return
