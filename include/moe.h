@@ -67,12 +67,21 @@ typedef enum moe_status {
     MOE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, aliasing */
     MOE_ERR_UNSUPPORTED = 2,      /* valid layer, but outside what the GPU path supports */
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-    MOE_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+    MOE_ERR_HIP = 4,              /* a HIP runtime call or launch failed */
+    /* range markers, not statuses: every int32 value is a valid moe_status_t
+     * (a C caller may pass any int to moe_status_string) */
+    MOE_STATUS_MIN_ENUM_ = -0x7fffffff - 1,
+    MOE_STATUS_MAX_ENUM_ = 0x7fffffff
 } moe_status_t;
 
 typedef enum moe_dtype {
     MOE_F32 = 0,  /* fp32 storage, fp32 arithmetic */
-    MOE_BF16 = 1  /* bf16 storage, fp32 accumulation */
+    MOE_BF16 = 1, /* bf16 storage, fp32 accumulation */
+    /* range markers, not dtypes: any int32 a caller passes is a valid
+     * moe_dtype_t value, which the calls then reject unless it is one of the
+     * two above */
+    MOE_DTYPE_MIN_ENUM_ = -0x7fffffff - 1,
+    MOE_DTYPE_MAX_ENUM_ = 0x7fffffff
 } moe_dtype_t;
 
 /* Stages of moe_forward / moe_block_forward and of moe_backward, in launch
@@ -116,8 +125,9 @@ moe_status_t moe_permute(const int32_t* idx, int64_t T, int32_t n, int32_t K,
                          void* stream);
 
 /* Bytes of workspace that moe_forward and moe_block_forward need for these
- * sizes.  An upper bound that does not depend on how tokens get routed.
- * Returns 0 if the sizes are invalid. */
+ * sizes.  An upper bound that does not depend on how tokens get routed.  For
+ * bf16 calls larger than one pass (see moe_forward) it is the workspace of one
+ * chunk, so it stops growing with T.  Returns 0 if the sizes are invalid. */
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n,
                            int32_t K, moe_dtype_t dt);
 
@@ -125,7 +135,19 @@ size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n,
  * "Method" section).  workspace: device memory of at least
  * moe_workspace_bytes(...) bytes, 256-byte aligned.  Optional outputs (NULL to
  * skip): idx_out[T][K], gate_out[T][K] -- the routing that was used -- and
- * counts_out[n], the number of assignments each expert received. */
+ * counts_out[n], the number of assignments each expert received.  The
+ * workspace must not overlap any other argument.
+ *
+ * The kernels index one pass's operands with 32-bit offsets: bf16 needs
+ * T * d and T * K * d_ff below 2^30 elements (T <= 37449 at d = 4096,
+ * d_ff = 14336, K = 2), fp32 needs T * K < 64 (65535 - n).  A call with more
+ * tokens runs them in the fewest near-equal chunks that fit, one after the
+ * other on `stream`, each chunk a whole layer pass over its own tokens (every
+ * token is routed and computed on its own, so y, idx_out and gate_out equal
+ * those of separate calls on the chunks; counts_out is their sum).  The
+ * expert weights themselves must fit (bf16: d * d_ff < 2^30 per expert),
+ * else MOE_ERR_UNSUPPORTED.  Stage events (moe_set_stage_events) then mark
+ * the last chunk. */
 moe_status_t moe_forward(const void* x, const void* w_g, const void* w1,
                          const void* w3, const void* w2, int64_t T, int64_t d,
                          int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,
@@ -189,8 +211,11 @@ size_t moe_backward_workspace_bytes(int64_t T, int64_t d, int64_t d_ff,
  * activation, g dy and the SwiGLU input gradients are rounded to bf16 before
  * the products that consume them.  workspace: at least
  * moe_backward_workspace_bytes(...) bytes, 256-byte aligned.  dt = MOE_F32
- * returns MOE_ERR_UNSUPPORTED.  T = 0 zeroes the weight gradients (x, dy and
- * dx may then be NULL).  Weight gradients are cleared with kernels, never a
+ * returns MOE_ERR_UNSUPPORTED.  One pass only: T * d, T * K * 2 d_ff and the
+ * expert weights must stay below 2^30 elements (T <= 18724 at d = 4096,
+ * d_ff = 14336, K = 2), else MOE_ERR_UNSUPPORTED; larger batches are split by
+ * the caller, who sums the weight gradients.  T = 0 zeroes the weight
+ * gradients (x, dy and dx may then be NULL).  Weight gradients are cleared with kernels, never a
  * memset, so the call can be captured into a HIP graph. */
 moe_status_t moe_backward(const void* x, const void* w_g, const void* w1,
                           const void* w3, const void* w2, const void* dy,
@@ -227,7 +252,9 @@ size_t moe_saved_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
  * assignment kept in `saved` (caller-owned device memory of at least
  * moe_saved_bytes(...) bytes, 256-byte aligned, opaque layout) for
  * moe_backward_saved, which then need not recompute them.  bf16 plain layer
- * only (MOE_ERR_UNSUPPORTED otherwise).  workspace as for moe_forward. */
+ * only (MOE_ERR_UNSUPPORTED otherwise).  workspace as for moe_forward.  One
+ * pass only: T beyond what one pass of moe_forward holds returns
+ * MOE_ERR_UNSUPPORTED (the saved state covers all T tokens at once). */
 moe_status_t moe_forward_train(const void* x, const void* w_g, const void* w1,
                                const void* w3, const void* w2, int64_t T, int64_t d,
                                int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt,

@@ -144,6 +144,28 @@ Layout layout(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtyp
     return L;
 }
 
+// Tokens per chunk of moe_forward / moe_block_forward: the most tokens whose
+// operands the kernels index with 32-bit offsets (bf16: T * d and T * K * d_ff
+// elements below 2^30; fp32: a grid bound of the grouped kernel).  A call with
+// more tokens runs them in near-equal chunks of at most this many, one after
+// the other on its stream, in a workspace sized for one chunk.  0: the weights
+// themselves are too large for the kernels.
+int64_t chunk_tokens(int64_t d, int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt) {
+    if (dt != MOE_BF16) return ((int64_t)65535 - n) * 64 / K;
+    if (!moe::tiled_fits(1, d, d_ff) || !moe::tiled_fits(K, d_ff, d)) return 0;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    const int64_t t1 = lim / (2 * d), t2 = lim / (2 * d_ff) / K;
+    return t1 < t2 ? t1 : t2;
+}
+
+// The chunk length of a call over T tokens: T itself when it fits, else
+// ceil(T / chunks) for the fewest chunks of at most chunk_tokens tokens.
+int64_t chunk_len(int64_t T, int64_t cmax) {
+    if (cmax <= 0 || T <= cmax) return T;
+    const int64_t chunks = (T + cmax - 1) / cmax;
+    return (T + chunks - 1) / chunks;
+}
+
 moe_status_t check_sizes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
                          moe_dtype_t dt, bool need_ff) {
     if (dt != MOE_F32 && dt != MOE_BF16)
@@ -293,85 +315,17 @@ moe_status_t scratch_address(void** out) {
     return MOE_OK;
 }
 
-moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
-                           const void* w3, const void* w2, int64_t T, int64_t d,
-                           int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, float eps,
-                           void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
-                           float* gate_out, int32_t* counts_out, void* stream,
-                           void* saved = nullptr, size_t saved_bytes = 0,
-                           bool static_scratch = false) {
-    const char* fn = static_scratch ? "moe_forward_noalloc"
-                     : saved ? (block ? "moe_block_forward_train" : "moe_forward_train")
-                             : block ? "moe_block_forward" : "moe_forward";
-    moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
-    if (st != MOE_OK) return st;
-    if (saved) {
-        if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
-        if (!aligned(saved, 256))
-            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
-        if (saved_bytes < saved_bytes_for(T, d, d_ff, n, K))
-            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: saved %zu bytes < %zu needed", fn,
-                        saved_bytes, saved_bytes_for(T, d, d_ff, n, K));
-    }
-    if (block && !(eps >= 0.0f && eps < 1e30f))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
-    const void* ptrs[] = {x, w_g, w1, w3, w2, y};
-    const char* names[] = {"x", "w_g", "w1", "w3", "w2", "y"};
-    for (int i = 0; i < 6; ++i) {
-        // x and y hold T rows: with T = 0 they may be NULL
-        if (!ptrs[i] && T == 0 && (i == 0 || i == 5)) continue;
-        if (!ptrs[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
-        if (!aligned(ptrs[i], 16))
-            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
-    }
-    if ((idx_out && !aligned(idx_out, 4)) || (gate_out && !aligned(gate_out, 4)) ||
-        (counts_out && !aligned(counts_out, 4)))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: optional outputs must be 4-byte aligned", fn);
-    if (dt == MOE_F32 && (int64_t)T * K / 64 + n > 65535)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 path supports T * K < 4M", fn);
-    if (dt == MOE_BF16 && (!moe::tiled_fits(T, d, d_ff) || !moe::tiled_fits((int64_t)T * K, d_ff, d)))
-        return fail(MOE_ERR_UNSUPPORTED,
-                    "%s: bf16 operands must stay below 2 GiB (T*d, T*K*d_ff, d*d_ff elements "
-                    "< 2^30); split the tokens into several calls",
-                    fn);
+// One pass of the layer over T tokens (at most chunk_tokens): router,
+// permutation, the two grouped GEMMs and the combine, launched on `stream`.
+// counts_mode: 0 = the permutation writes counts_out; 1 / 2 = the first /
+// a later chunk of a chunked call (counts_out set / summed from the offsets).
+moe_status_t forward_pass(bool block, const void* x, const void* w_g, const void* w1,
+                          const void* w3, const void* w2, int64_t T, int64_t d, int64_t d_ff,
+                          int32_t n, int32_t K, moe_dtype_t dt, float eps, void* y,
+                          void* workspace, int32_t* idx_out, float* gate_out,
+                          int32_t* counts_out, int counts_mode, void* stream, void* saved) {
     const Layout L = layout(T, d, d_ff, n, K, dt);
-    if (static_scratch && L.total > kScratchBytes)
-        return fail(MOE_ERR_UNSUPPORTED,
-                    "%s: these sizes need %zu bytes of scratch, the library's static scratch "
-                    "holds %zu (enough for 256 tokens at d = 4096, d_ff = 14336, n = 8, K = 2); "
-                    "call moe_forward with a workspace instead",
-                    fn, L.total, kScratchBytes);
-    if (T > 0 && !static_scratch) {
-        if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
-        if (!aligned(workspace, 256))
-            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
-        if (ws_bytes < L.total)
-            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", fn,
-                        ws_bytes, L.total);
-    }
-    const size_t es = dt == MOE_BF16 ? 2 : 4;
     const size_t A = (size_t)T * (size_t)K;
-    const size_t ybytes = (size_t)T * (size_t)d * es;
-    const size_t wbytes = (size_t)n * (size_t)d_ff * (size_t)d * es;
-    if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, w_g, (size_t)d * n * es) ||
-        overlaps(y, ybytes, w1, wbytes) || overlaps(y, ybytes, w3, wbytes) ||
-        overlaps(y, ybytes, w2, wbytes) || overlaps(y, ybytes, workspace, L.total) ||
-        overlaps(y, ybytes, idx_out, A * 4) || overlaps(y, ybytes, gate_out, A * 4) ||
-        overlaps(y, ybytes, counts_out, (size_t)n * 4) || overlaps(y, ybytes, saved, saved_bytes))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: y overlaps another argument", fn);
-    if (saved) {
-        const void* others[] = {x, w_g, w1, w3, w2, workspace};
-        const size_t osz[] = {ybytes, (size_t)d * n * es, wbytes, wbytes, wbytes, L.total};
-        for (int i = 0; i < 6; ++i)
-            if (overlaps(saved, saved_bytes, others[i], osz[i]))
-                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved overlaps another argument", fn);
-    }
-    if (T == 0) return MOE_OK;
-    if (static_scratch) {
-        st = scratch_address(&workspace);
-        if (st != MOE_OK) return st;
-    }
-
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
@@ -397,7 +351,6 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     const bool bf16 = dt == MOE_BF16;
     const Plan plan = choose_plan(T, d, d_ff, n, K, dt);
 
-    (void)hipGetLastError();  // clear a stale error so launch checks report our own
     hipError_t err = hipSuccess;
     auto mark = [&](hipEvent_t ev) {
         if (ev && err == hipSuccess) err = hipEventRecord(ev, s);
@@ -409,8 +362,11 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     if (err != hipSuccess) return hip_fail(err, "router launch");
     mark(g_ev_start[MOE_STAGE_PERMUTE]);
     if (err == hipSuccess)
-        err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv, counts_out, s,
+        err = moe::launch_permute(idx, (int64_t)A, n, offsets, perm, inv,
+                                  counts_mode == 0 ? counts_out : nullptr, s,
                                   reinterpret_cast<int32_t*>(ws + L.pcnt));
+    if (err == hipSuccess && counts_mode != 0 && counts_out)
+        err = moe::launch_add_counts(offsets, n, counts_mode == 1, counts_out, s);
     mark(g_ev_end[MOE_STAGE_PERMUTE]);
     if (err != hipSuccess) return hip_fail(err, "permute launch");
     const void* act = block ? u : x;
@@ -472,6 +428,111 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
                                   y, split_meta, s);
     mark(g_ev_end[MOE_STAGE_COMBINE]);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return MOE_OK;
+}
+
+
+moe_status_t layer_forward(bool block, const void* x, const void* w_g, const void* w1,
+                           const void* w3, const void* w2, int64_t T, int64_t d,
+                           int64_t d_ff, int32_t n, int32_t K, moe_dtype_t dt, float eps,
+                           void* y, void* workspace, size_t ws_bytes, int32_t* idx_out,
+                           float* gate_out, int32_t* counts_out, void* stream,
+                           void* saved = nullptr, size_t saved_bytes = 0,
+                           bool static_scratch = false) {
+    const char* fn = static_scratch ? "moe_forward_noalloc"
+                     : saved ? (block ? "moe_block_forward_train" : "moe_forward_train")
+                             : block ? "moe_block_forward" : "moe_forward";
+    moe_status_t st = check_sizes(T, d, d_ff, n, K, dt, true);
+    if (st != MOE_OK) return st;
+    if (saved) {
+        if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+        if (!aligned(saved, 256))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved is not 256-byte aligned", fn);
+        if (saved_bytes < saved_bytes_for(T, d, d_ff, n, K))
+            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: saved %zu bytes < %zu needed", fn,
+                        saved_bytes, saved_bytes_for(T, d, d_ff, n, K));
+    }
+    if (block && !(eps >= 0.0f && eps < 1e30f))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    const void* ptrs[] = {x, w_g, w1, w3, w2, y};
+    const char* names[] = {"x", "w_g", "w1", "w3", "w2", "y"};
+    for (int i = 0; i < 6; ++i) {
+        // x and y hold T rows: with T = 0 they may be NULL
+        if (!ptrs[i] && T == 0 && (i == 0 || i == 5)) continue;
+        if (!ptrs[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
+        if (!aligned(ptrs[i], 16))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
+    }
+    if ((idx_out && !aligned(idx_out, 4)) || (gate_out && !aligned(gate_out, 4)) ||
+        (counts_out && !aligned(counts_out, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: optional outputs must be 4-byte aligned", fn);
+    const int64_t cmax = chunk_tokens(d, d_ff, n, K, dt);
+    if (cmax <= 0)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: bf16 expert weights must stay below 2 GiB (d * d_ff < 2^30)", fn);
+    // the saved training state and the static scratch hold one pass over all T tokens
+    if ((saved || static_scratch) && T > cmax)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: %lld tokens exceed the %lld one pass can index (operands below 2 GiB); "
+                    "split the tokens into several calls",
+                    fn, (long long)T, (long long)cmax);
+    const int64_t Tc = chunk_len(T, cmax);  // tokens per chunk (T when one pass fits)
+    const Layout L = layout(Tc, d, d_ff, n, K, dt);
+    if (static_scratch && L.total > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: these sizes need %zu bytes of scratch, the library's static scratch "
+                    "holds %zu (enough for 256 tokens at d = 4096, d_ff = 14336, n = 8, K = 2); "
+                    "call moe_forward with a workspace instead",
+                    fn, L.total, kScratchBytes);
+    if (T > 0 && !static_scratch) {
+        if (!workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is NULL", fn);
+        if (!aligned(workspace, 256))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", fn);
+        if (ws_bytes < L.total)
+            return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", fn,
+                        ws_bytes, L.total);
+    }
+    const size_t es = dt == MOE_BF16 ? 2 : 4;
+    const size_t A = (size_t)T * (size_t)K;
+    const size_t ybytes = (size_t)T * (size_t)d * es;
+    const size_t wbytes = (size_t)n * (size_t)d_ff * (size_t)d * es;
+    if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, w_g, (size_t)d * n * es) ||
+        overlaps(y, ybytes, w1, wbytes) || overlaps(y, ybytes, w3, wbytes) ||
+        overlaps(y, ybytes, w2, wbytes) || overlaps(y, ybytes, workspace, L.total) ||
+        overlaps(y, ybytes, idx_out, A * 4) || overlaps(y, ybytes, gate_out, A * 4) ||
+        overlaps(y, ybytes, counts_out, (size_t)n * 4) || overlaps(y, ybytes, saved, saved_bytes))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: y overlaps another argument", fn);
+    if (saved) {
+        const void* others[] = {x, w_g, w1, w3, w2, workspace};
+        const size_t osz[] = {ybytes, (size_t)d * n * es, wbytes, wbytes, wbytes, L.total};
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(saved, saved_bytes, others[i], osz[i]))
+                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: saved overlaps another argument", fn);
+    }
+    if (!static_scratch) {  // the kernels write the workspace while reading the inputs
+        const void* others[] = {x, w_g, w1, w3, w2, idx_out, gate_out, counts_out, saved};
+        const size_t osz[] = {ybytes, (size_t)d * n * es, wbytes, wbytes, wbytes, A * 4, A * 4,
+                              (size_t)n * 4, saved_bytes};
+        for (int i = 0; i < 9; ++i)
+            if (overlaps(workspace, L.total, others[i], osz[i]))
+                return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace overlaps another argument",
+                            fn);
+    }
+    if (T == 0) return MOE_OK;
+    if (static_scratch) {
+        st = scratch_address(&workspace);
+        if (st != MOE_OK) return st;
+    }
+    (void)hipGetLastError();  // clear a stale error so launch checks report our own
+    for (int64_t c0 = 0; c0 < T; c0 += Tc) {
+        const int64_t t = T - c0 < Tc ? T - c0 : Tc;
+        const size_t xo = (size_t)c0 * (size_t)d * es, ao = (size_t)c0 * (size_t)K;
+        st = forward_pass(block, static_cast<const char*>(x) + xo, w_g, w1, w3, w2, t, d, d_ff, n,
+                          K, dt, eps, static_cast<char*>(y) + xo, workspace,
+                          idx_out ? idx_out + ao : nullptr, gate_out ? gate_out + ao : nullptr,
+                          counts_out, Tc < T ? (c0 == 0 ? 1 : 2) : 0, stream, saved);
+        if (st != MOE_OK) return st;
+    }
     g_last_error[0] = '\0';
     return MOE_OK;
 }
@@ -705,8 +766,8 @@ const char* moe_status_string(moe_status_t st) {
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
         case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
     }
-    return "MOE_ERR_UNKNOWN";
 }
 
 const char* moe_last_error(void) { return g_last_error; }
@@ -714,7 +775,7 @@ const char* moe_last_error(void) { return g_last_error; }
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t d_ff, int32_t n, int32_t K,
                            moe_dtype_t dt) {
     if (check_sizes(T, d, d_ff, n, K, dt, true) != MOE_OK) return 0;
-    return layout(T, d, d_ff, n, K, dt).total;
+    return layout(chunk_len(T, chunk_tokens(d, d_ff, n, K, dt)), d, d_ff, n, K, dt).total;
 }
 
 moe_status_t moe_route(const void* x, const void* w_g, int64_t T, int64_t d, int32_t n,

@@ -140,6 +140,9 @@ hipError_t launch_bwd_dwg(const uint16_t* x, const float* scale, const float* dl
                           int d, int n, float* part, float* dwg, hipStream_t s);
 // Zero `bytes` (a multiple of 16) at p with a kernel.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// counts[e] = offsets[e + 1] - offsets[e] (first) or counts[e] += that (n <= 64).
+hipError_t launch_add_counts(const int32_t* offsets, int n, bool first, int32_t* counts,
+                             hipStream_t s);
 // XG[p] = x[perm[p] / K] and YG[p] = y[perm[p] / K] (bf16 rows of d
 // elements), p < A.
 hipError_t launch_gather_rows(const uint16_t* x, const uint16_t* y, const int32_t* perm, int K,

@@ -151,6 +151,22 @@ int permute_blocks(int64_t A) {
     return (int)((A + ch - 1) / ch);
 }
 
+// counts[e] (+)= offsets[e + 1] - offsets[e]: the per-expert counts of a call
+// that runs its tokens in several chunks, summed chunk after chunk in stream
+// order (one thread per expert, no atomics).
+__global__ void add_counts_kernel(const int32_t* __restrict__ offsets, int n, int first,
+                                  int32_t* __restrict__ counts) {
+    const int e = threadIdx.x;
+    if (e < n) counts[e] = (first ? 0 : counts[e]) + (offsets[e + 1] - offsets[e]);
+}
+
+hipError_t launch_add_counts(const int32_t* offsets, int n, bool first, int32_t* counts,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(add_counts_kernel, dim3(1), dim3(64), 0, s, offsets, n, first ? 1 : 0,
+                       counts);
+    return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* idx, int64_t A, int n, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* counts, hipStream_t s,
                           int32_t* scratch) {

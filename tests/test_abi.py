@@ -63,6 +63,64 @@ def test_workspace_bytes_bounds(lib):
     assert lib.moe_workspace_bytes(16, d, d_ff, 8, 2, 7) == 0
 
 
+def _one_pass_tokens(d, d_ff, n, K, bf16=True):
+    """Most tokens one pass of the layer indexes with 32-bit offsets: bf16
+    operands T*d and T*K*d_ff below 2^30 elements; fp32 T*K below 64 (65535 - n)."""
+    if not bf16:
+        return (65535 - n) * 64 // K
+    lim = (1 << 31) - 1
+    return min(lim // (2 * d), lim // (2 * d_ff) // K)
+
+
+@pytest.mark.parametrize("d,d_ff,n,K,bf16", [(4096, 14336, 8, 2, True), (128, 32768, 8, 2, True),
+                                            (4096, 14336, 8, 1, True), (64, 64, 8, 2, False),
+                                            (8192, 4096, 16, 4, True)])
+def test_workspace_bound_stops_at_one_chunk(lib, d, d_ff, n, K, bf16):
+    """Above one pass, moe_forward runs near-equal chunks of at most
+    _one_pass_tokens tokens in a workspace sized for one chunk."""
+    dt = B.MOE_BF16 if bf16 else B.MOE_F32
+    cmax = _one_pass_tokens(d, d_ff, n, K, bf16)
+    ws = lambda T: lib.moe_workspace_bytes(T, d, d_ff, n, K, dt)
+    assert ws(cmax) > ws(cmax - 1) > 0
+    assert ws(cmax + 1) == ws((cmax + 2) // 2) < ws(cmax)   # two chunks
+    for T in (2 * cmax, 2 * cmax + 1, 5 * cmax + 7, (1 << 30) // K - 1):
+        chunks = -(-T // cmax)
+        assert ws(T) == ws(-(-T // chunks)) <= ws(cmax), T
+
+
+def test_one_pass_calls_refuse_larger_batches(lib):
+    """The training pair and the backward hold all T tokens in one pass;
+    the static scratch of moe_forward_noalloc is smaller still."""
+    d, d_ff, n, K = 4096, 14336, 8, 2
+    T = _one_pass_tokens(d, d_ff, n, K) + 1
+    sb = lib.moe_saved_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    st = lib.moe_forward_train(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d, d_ff, n, K,
+                               B.MOE_BF16, 1 << 44, 1 << 45, sb, 1 << 46, 1 << 40, None)
+    assert st == B.MOE_ERR_UNSUPPORTED and b"split the tokens" in lib.moe_last_error()
+    st = lib.moe_forward_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, T, d, d_ff, n,
+                                 K, B.MOE_BF16, 1 << 44, None, None, None, None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    # weights past 2 GiB per expert cannot be chunked
+    assert _fwd(lib, d=16384, d_ff=65536, ws_bytes=1 << 40) == B.MOE_ERR_UNSUPPORTED
+    assert b"d * d_ff" in lib.moe_last_error()
+
+
+def test_chunked_forward_validates_the_whole_call(lib):
+    """A chunked call checks every argument over all T tokens before it
+    enqueues anything (the workspace only needs one chunk's bytes)."""
+    d, d_ff, n, K = 128, 32768, 8, 2
+    T = 3 * _one_pass_tokens(d, d_ff, n, K) + 5
+    need = lib.moe_workspace_bytes(T, d, d_ff, n, K, B.MOE_BF16)
+    base = dict(T=T, d=d, d_ff=d_ff, n=n, K=K, x=1 << 40, y=1 << 41, ws=1 << 42, ws_bytes=need)
+    assert _fwd(lib, **dict(base, ws_bytes=need - 1)) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # idx_out of all T tokens reaching into the workspace
+    st = _fwd(lib, **dict(base, idx=(1 << 42) - T * K * 4 + 256))
+    assert st == B.MOE_ERR_INVALID_ARGUMENT and b"workspace overlaps" in lib.moe_last_error()
+    # y of all T tokens reaching into the workspace
+    st = _fwd(lib, **dict(base, y=(1 << 42) - T * d * 2 + 256))
+    assert st == B.MOE_ERR_INVALID_ARGUMENT and b"overlaps" in lib.moe_last_error()
+
+
 FAKE = 0x10000  # 16-byte and 256-byte aligned, never dereferenced by validation
 
 
