@@ -140,19 +140,24 @@ def cpu_baseline(w, L, budget_s: float):
     t0 = time.perf_counter()
     run(probe)
     per_tok = (time.perf_counter() - t0) / len(probe)
-    n_tok = max(1, int(budget_s / max(per_tok, 1e-9)))
     reps, tokens, elapsed = 0, 0, 0.0
-    while elapsed < budget_s or reps == 0:
+    # each call takes distinct tokens (at most all T), sized from the measured
+    # per-token time to fill what is left of the budget
+    while elapsed < 0.9 * budget_s or reps == 0:
+        n_tok = max(1, int((budget_s - elapsed) / max(per_tok, 1e-9)))
         rows = np.sort(rng.choice(w.T, min(w.T, n_tok), replace=False))
         t0 = time.perf_counter()
         run(rows)
-        elapsed += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        per_tok = dt / len(rows)
         tokens += len(rows)
         reps += 1
     if tokens == w.T * reps:
         sample = f"all {w.T} tokens of the workload x{reps}"
     else:
-        sample = f"{tokens} tokens drawn from the workload's {w.T} ({reps} oracle call(s))"
+        sample = (f"{tokens} tokens in {reps} oracle call(s), each on distinct tokens drawn "
+                  f"from the workload's {w.T}")
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2),
             "cpu": cpu_model()}
