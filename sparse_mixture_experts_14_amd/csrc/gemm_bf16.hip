@@ -32,11 +32,14 @@
 //
 // Pipeline.  Two LDS stages of 64-deep A and B tiles (rows of 128 bytes, the
 // 16-byte chunk XOR-swizzled by (row / 2) % 8 so that the fragment reads of
-// 16 consecutive rows hit distinct banks).  A stage is filled by buffer loads
-// with the LDS flag (global -> LDS, no registers, no LDS write instructions),
-// issued one step ahead among the MFMAs of the first two sub-steps of a step;
-// one barrier per step waits for them (four-wave square tiles also prefetch
-// their weight rows into L2 two steps ahead).  Rows past the tile are clamped
+// 16 consecutive rows hit distinct banks).  Gate/up and the backward fill a
+// stage with buffer loads with the LDS flag (global -> LDS, no registers, no
+// LDS write instructions), issued one step ahead among the MFMAs of the first
+// two sub-steps of a step; one barrier per step waits for them (four-wave
+// square gate/up tiles also prefetch their weight rows into L2 two steps
+// ahead).  The down projection's four-wave tiles stage through registers
+// instead: loads in address order two steps ahead, LDS writes to the
+// swizzled slots one step ahead, spread over three sub-steps.  Rows past the tile are clamped
 // to a valid row (never stored); a K tail and the step past the end load
 // through an out-of-range offset, which writes zeros.  Outputs leave through
 // LDS as whole 16-byte
@@ -153,7 +156,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wid % WM, wn = wid / WM;
 
-    // ---- loader: global -> LDS without registers -----------------------------
+    // ---- loader: global -> LDS (directly, or through staging registers) -------
     // A buffer load with the LDS flag writes lane l's 16 bytes at LDS address
     // M0 + 16 l, so one instruction fills 1 KB = ROWS_LD consecutive LDS rows.
     // Lane l serves row ROWS_LD q + l / CH and physical chunk l % CH, i.e. the
@@ -166,6 +169,14 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     static_assert(A_LD * 1024 * NW == BM * KD * 2 && B_LD * 1024 * NW == BN * KD * 2,
                   "loader split");
     static_assert(!GATEUP || B_LD % 2 == 0, "W1 and W3 halves of the B tile");
+    // Register-staged loads (the down projection's four-wave tiles): each
+    // lane loads its chunk in natural order (lane l: row l / CH, chunk l % CH,
+    // so the CH lanes of a row read its 128 bytes in address order) into
+    // VGPRs two K steps ahead, and writes it to its swizzled LDS slot one
+    // step later.  Measured A/B in one process, bitwise-identical output:
+    // down -9..-12% (prefill, skew, stack layer).  On gate/up it was neutral
+    // (within 1.5%), and gate/up keeps the direct loads and the L2 touch.
+    constexpr bool RSTAGE = !GATEUP && !AKR && !BKR && NW == 4;
     const int rr = lane / CH, pc = lane % CH;
     const uint32_t src_row_bytes = (uint32_t)Kdim * 2u;
     const __amdgpu_buffer_rsrc_t a_rs = rsrc(t.A, t.A_src_rows * (int64_t)Kdim * 2);
@@ -185,7 +196,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int r = a_lrow(i) + rr;
-        const int c = pc ^ ((r / RPB) % CH);
+        const int c = RSTAGE ? pc : pc ^ ((r / RPB) % CH);
         const int p = t.row0 + min(r, rows - 1);  // rows past the tile: a valid row, never stored
         const uint32_t src = GATEUP ? (uint32_t)(t.perm[p] / t.K) : (uint32_t)p;
         a_off[i] = src * src_row_bytes + (uint32_t)c * 16u;
@@ -194,7 +205,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
         const int r = b_lrow(i) + rr;
-        const int c = pc ^ ((r / RPB) % CH);
+        const int c = RSTAGE ? pc : pc ^ ((r / RPB) % CH);
         const int col = n0 + (GATEUP && r >= BN / 2 ? r - BN / 2 : r);
         b_off[i] = (uint32_t)min(col, N - 1) * src_row_bytes + (uint32_t)c * 16u;
         b_k8[i] = c * 8;
@@ -241,6 +252,51 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // zero-size resource: every load is out of range and writes zeros, so the
     // issue pattern and the load count stay the same.  K tails: chunks past
     // Kdim get an out-of-range offset.
+    // Register staging: loads lo .. hi - 1 of K step kt into the staging
+    // registers (a step past the end reads zeros through the zero-size
+    // resource), and the staged loads lo .. hi - 1 written to stage `st` at
+    // the swizzled slot of their (row, chunk).
+    u32x4_t ra[RSTAGE ? A_LD : 1], rb[RSTAGE ? B_LD : 1];
+    auto gload = [&](int kt, int lo, int hi) {
+        if constexpr (RSTAGE) {
+            const bool live = kt < k_end;
+            const int k0 = live ? kt * BK : 0;
+            const __amdgpu_buffer_rsrc_t ars = live ? a_rs : null_rs;
+            const __amdgpu_buffer_rsrc_t brs = live ? b1_rs : null_rs;
+#pragma unroll
+            for (int i = 0; i < A_LD; ++i) {
+                if (i < lo || i >= hi) continue;
+                const uint32_t off = KTAIL && k0 + a_k8[i] >= Kdim ? 0x80000000u : a_off[i];
+                ra[i] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)off, k0 * 2, 0));
+            }
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i) {
+                if (A_LD + i < lo || A_LD + i >= hi) continue;
+                const uint32_t off = KTAIL && k0 + b_k8[i] >= Kdim ? 0x80000000u : b_off[i];
+                rb[i] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, (int)off, k0 * 2, 0));
+            }
+        }
+    };
+    auto sstore = [&](uint8_t* st, int lo, int hi) {
+        if constexpr (RSTAGE) {
+#pragma unroll
+            for (int i = 0; i < A_LD; ++i) {
+                if (i < lo || i >= hi) continue;
+                const int r = a_lrow(i) + rr;
+                *reinterpret_cast<u32x4_t*>(st + r * ROW_BYTES + ((pc ^ ((r / RPB) % CH)) << 4)) =
+                    ra[i];
+            }
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i) {
+                if (A_LD + i < lo || A_LD + i >= hi) continue;
+                const int r = b_lrow(i) + rr;
+                *reinterpret_cast<u32x4_t*>(st + A_BYTES + r * ROW_BYTES +
+                                            ((pc ^ ((r / RPB) % CH)) << 4)) = rb[i];
+            }
+        }
+    };
     // Loads lo .. hi - 1 of the step's NLD (A loads first, then B loads).
     auto issue = [&](uint8_t* st, int kt, int lo = 0, int hi = 1 << 30) {
         const bool live = kt < k_end;
@@ -306,7 +362,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // vmcnt(1) leaves exactly that load outstanding.  Measured: gate/up 2-4%
     // faster, the four-wave down projection 4-5% (on the eight-wave one it
     // was slower).
-    constexpr bool TOUCH = SH::BM == 256 && SH::BN == 256 && NW == 4 && !AKR && !BKR;
+    constexpr bool TOUCH = SH::BM == 256 && SH::BN == 256 && NW == 4 && !AKR && !BKR && !RSTAGE;
     auto touch = [&](int kt2) -> uint32_t {
         if constexpr (TOUCH) {
             const int r = wid * 64 + lane;  // B tile row (gate/up: W1 rows, then W3 rows)
@@ -406,9 +462,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // read): the LDS reads of the next sub-step go out one per MFMA at the
     // start of a sub-step, so their latency hides behind the remaining MFMAs;
     // the first sub-step of a step also carries the next step's loads (LPM
-    // per MFMA).
+    // per MFMA).  Register staging instead puts one LDS write, then one load,
+    // on every third MFMA: bunched writes filled the LDS data FIFO and
+    // stalled the wave (every third MFMA measured 2-3% faster than every
+    // other, and 7-11% faster than one per MFMA).
     constexpr int NRD = (AKR ? 2 : 1) * TM + (BKR ? 2 : 1) * TN;  // LDS reads per sub-step
-    auto interleave = [&](int nloads) {
+    auto interleave = [&](int nloads, int nwrites = 0) {
         constexpr int LPM = (NLD + TM * TN - 1) / (TM * TN);
         constexpr int RPM = (NRD + TM * TN - 1) / (TM * TN);
 #pragma unroll
@@ -416,17 +475,28 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
 #pragma unroll
             for (int r = 0; r < RPM; ++r)
                 if (q * RPM + r < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (nwrites > 0) {
+                if (q % 3 == 0 && q / 3 < nwrites) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (q % 3 == 2 && q / 3 < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            } else {
 #pragma unroll
-            for (int r = 0; r < LPM; ++r)
-                if (q * LPM + r < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                for (int r = 0; r < LPM; ++r)
+                    if (q * LPM + r < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     };
     // Block-wide barrier that waits for this wave's loads (the step about to
     // be read) and its own LDS reads (the stage they read is refilled next);
     // the youngest load, an L2 prefetch, may stay in flight.
+    // With register staging nothing of the step about to be read is in
+    // flight (its data went through VGPRs), and the staged loads stay in
+    // flight across the barrier.
     auto barrier = [&]() {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(TOUCH ? 1 : 0, 0));
+        if constexpr (RSTAGE)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(TOUCH ? 1 : 0, 0));
         __builtin_amdgcn_s_barrier();
         __asm__ __volatile__("" ::: "memory");
     };
@@ -442,7 +512,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // MFMAs (FIFO-full stall counters 10x those of hipBLASLt's kernel on the
     // same product).  Measured: gate/up 3.3-6.7% faster; the eight-wave
     // tiles, whose SIMDs hold a second wave, were not.
-    constexpr int SPREAD = NW == 4 && KS > 2 ? 2 : 1;
+    // Register staging spreads over sub-steps 1 .. KS - 1 instead: in each,
+    // part of stage Y is written from the staging registers (step kt + 1,
+    // loaded during step kt - 1), and the same registers are then reloaded
+    // with that part of step kt + 2.
+    constexpr int SPREAD = RSTAGE ? KS - 1 : NW == 4 && KS > 2 ? 2 : 1;
     bf16x8_t fa[2][TM], fb[2][TN];
     auto step = [&](const uint8_t* X, uint8_t* Y, int kt) {
         uint32_t touch_now = 0;
@@ -450,10 +524,17 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         for (int sub = 1; sub < KS; ++sub) {
             const int lo = sub <= SPREAD ? (sub - 1) * NLD / SPREAD : NLD;
             const int hi = sub <= SPREAD ? sub * NLD / SPREAD : NLD;
-            if (hi > lo) issue(Y, kt + 1, lo, hi);
+            if constexpr (RSTAGE) {
+                if (hi > lo) {
+                    sstore(Y, lo, hi);
+                    gload(kt + 2, lo, hi);
+                }
+            } else if (hi > lo) {
+                issue(Y, kt + 1, lo, hi);
+            }
             read_frags(X, sub, fa[sub & 1], fb[sub & 1]);
             mfmas(fa[(sub - 1) & 1], fb[(sub - 1) & 1]);
-            interleave(hi - lo);
+            interleave(hi - lo, RSTAGE ? hi - lo : 0);
             __builtin_amdgcn_sched_barrier(0);
             if (TOUCH && sub == SPREAD) {  // after every stage load of the step
                 touch_now = touch(kt + 2);
@@ -470,7 +551,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(S0, t.k_begin);
+    if constexpr (RSTAGE) {
+        gload(t.k_begin, 0, NLD);
+        sstore(S0, 0, NLD);
+        gload(t.k_begin + 1, 0, NLD);
+    } else {
+        issue(S0, t.k_begin);
+    }
     if constexpr (TOUCH) {
         __builtin_amdgcn_sched_barrier(0);
         touched = touch(t.k_begin + 1);
@@ -483,7 +570,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
         step(S1, S0, kt + 1);
     }
     // Drain: the loads past the last step are out of range but still write
-    // LDS; wait for them before the stages are reused for staging.
+    // LDS (or staging registers); wait for them before the stages are reused
+    // for staging.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     if constexpr (TOUCH) __asm__ __volatile__("" ::"v"(touched));
 
