@@ -177,7 +177,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     // down -9..-12% (prefill, skew, stack layer).  On gate/up it was neutral
     // (within 1.5%), and gate/up keeps the direct loads and the L2 touch.
     constexpr bool RSTAGE = !GATEUP && !AKR && !BKR && NW == 4;
-    const int rr = lane / CH, pc = lane % CH;
+    // The lane's loader coordinates are recomputed for every tile from an
+    // opaque copy of the lane id: hoisted out of the kernel's tile loop they
+    // stayed live across the K loop and the epilogue, and the register
+    // allocator parked them in scratch (gate/up, 12 bytes per lane).
+    int lane_t = lane;
+    __asm__ __volatile__("" : "+v"(lane_t));
+    const int rr = lane_t / CH, pc = lane_t % CH;
     const uint32_t src_row_bytes = (uint32_t)Kdim * 2u;
     const __amdgpu_buffer_rsrc_t a_rs = rsrc(t.A, t.A_src_rows * (int64_t)Kdim * 2);
     const int64_t wbytes = (int64_t)N * Kdim * 2;
@@ -589,6 +595,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
     constexpr int SLOT = 32 * RSTRIDE;                       // one wave's staging slot
     static_assert(SLOT * (NW / 2) <= STG, "half the waves stage in each stage buffer");
     __syncthreads();  // every wave is done with the K-loop LDS
+    // the epilogue's lane coordinates, likewise from an opaque lane id (not
+    // kept from before the K loop)
+    int lane_e = lane;
+    __asm__ __volatile__("" : "+v"(lane_e));
+    const int l32e = lane_e & 31, khalfe = lane_e >> 5;
     uint8_t* slot = (wid < NW / 2 ? S0 : S1) + (wid % (NW / 2)) * (STG / (NW / 2));
     const int col_w = n0 + wn * OCOLS;  // first output column of this wave
     constexpr int CPR = OCOLS * ES / 16;      // 16-byte chunks per staged row
@@ -608,8 +619,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
             for (int j = 0; j < (GATEUP ? TN / 2 : TN); ++j) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c = j * 32 + 8 * q + 4 * khalf;  // column within the wave
-                    uint8_t* dst = slot + l32 * RSTRIDE + c * ES;
+                    const int c = j * 32 + 8 * q + 4 * khalfe;  // column within the wave
+                    uint8_t* dst = slot + l32e * RSTRIDE + c * ES;
                     if (GATEUP && !h_pass) {
                         const f32x16_t& v = acc[i][j + ab_half * (TN / 2)];
                         u32x2_t h;
@@ -643,7 +654,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& t, uint8_t* S0, uint8_
             // needed (also before the second half overwrites the slot).
 #pragma unroll
             for (int rr2 = 0; rr2 < 32; rr2 += RPI) {
-                const int r = rr2 + lane / CPR, ch = lane % CPR;
+                const int r = rr2 + lane_e / CPR, ch = lane_e % CPR;
                 const int row = wm * WTM + i * 32 + r;
                 const int col = col_w + ch * (16 / ES);
                 const u32x4_t v =

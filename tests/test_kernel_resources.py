@@ -3,12 +3,11 @@ repository's own sources (hipcc -S, no GPU needed).
 
 * No scratch (spill) instruction may sit inside a loop that issues MFMAs:
   such a loop is the kernel's hot path.
-* Every kernel has a zero private segment (no spills at all), except the two
-  gate/up variants whose epilogue evaluates SiLU (H, and H plus [a | b]).
-  Their main loop holds 100 VGPRs plus 256 accumulator AGPRs; the register
-  allocator parks one lane offset shared by the loader and the epilogue in
-  scratch once per tile (a store before the K loop, reloads in the epilogue),
-  which this test bounds to a few dwords.
+* Every kernel has a zero private segment (no spills at all), except the
+  training variant of gate/up that stores both H and the pre-activation rows
+  [a | b] (three epilogue passes): the register allocator parks one 64-bit
+  output base per lane in scratch once per tile (a store before the K loop,
+  reloads in the epilogue), which this test bounds to a few dwords.
 """
 import concurrent.futures
 import os
@@ -21,10 +20,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_14_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["gemm_bf16.hip", "gemm_skinny.hip", "gemm_krow_stream.hip", "backward.hip"]
-# kernels allowed a small private segment: gate/up with the SiLU epilogue
-# (template EPI 0: H; EPI 3: H and [a | b]); bytes per lane at most
-ALLOWED = {r"gemm_bf16_kernelILb1ELb[01]ELi4ELi0ELb0": 16,
-           r"gemm_bf16_kernelILb1ELb[01]ELi4ELi3ELb0": 32}
+# kernels allowed a small private segment: the gate/up that stores H and
+# [a | b] (template EPI 3); bytes per lane at most
+ALLOWED = {r"gemm_bf16_kernelILb1ELb[01]ELi4ELi3ELb0": 16}
 
 
 def _assemble(src, tmp):
@@ -112,4 +110,4 @@ def test_private_segments(assembly):
             limit = next((v for k, v in ALLOWED.items() if re.search(k, name)), 0)
             seen_gateup += limit > 0
             assert seg <= limit, f"{src} {name}: {seg} bytes of scratch per lane"
-    assert seen_gateup == 4
+    assert seen_gateup == 2
