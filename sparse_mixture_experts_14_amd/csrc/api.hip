@@ -473,9 +473,10 @@ moe_status_t layer_forward(bool block, const void* x, const void* w_g, const voi
     // the saved training state and the static scratch hold one pass over all T tokens
     if ((saved || static_scratch) && T > cmax)
         return fail(MOE_ERR_UNSUPPORTED,
-                    "%s: %lld tokens exceed the %lld one pass can index (operands below 2 GiB); "
-                    "split the tokens into several calls",
-                    fn, (long long)T, (long long)cmax);
+                    "%s: %lld tokens exceed the %lld one pass can index (%s); split the tokens "
+                    "into several calls",
+                    fn, (long long)T, (long long)cmax,
+                    dt == MOE_BF16 ? "bf16 operands below 2 GiB" : "the fp32 grid bound");
     const int64_t Tc = chunk_len(T, cmax);  // tokens per chunk (T when one pass fits)
     const Layout L = layout(Tc, d, d_ff, n, K, dt);
     if (static_scratch && L.total > kScratchBytes)
